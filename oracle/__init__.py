@@ -1,0 +1,44 @@
+"""CPU oracle for the Hadamard rotate + quantize path (TEST INFRASTRUCTURE ONLY).
+
+Plain, slow, obviously correct numpy code in float64 that computes what the
+GPU library computes, from the definitions on the pages:
+
+* the rotation is the explicit dense product y = x . R with R built as a
+  matrix (Sylvester Hadamard, block-diagonal Hadamard, or a Kronecker product
+  of a Paley base matrix and a Sylvester matrix), normalised to be orthogonal;
+* the quantizers (round-to-nearest integer groups, MXFP4) are evaluated
+  element by element with numpy's round-half-to-even.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  It shares no code with the HIP library and
+never imports it; the product path must not route through it.
+
+Parity status of each function is stated in its docstring.  One part is
+*parity unpinned* against the pages: the Paley base matrices used for widths
+that are not a power of two are this project's own construction (the pages'
+table of known matrices is not available); they are pinned to the
+mathematics (H_K . H_K^T = K I), not to the pages' matrices.
+"""
+from .hadamard import (  # noqa: F401
+    kron_factor,
+    paley_hadamard,
+    rotate,
+    rotation_matrix,
+    sylvester,
+    sylvester_entry,
+)
+from .quant import (  # noqa: F401
+    E2M1_VALUES,
+    QuantResult,
+    bf16_round,
+    dequant_int,
+    dequant_mxfp4,
+    e2m1_round,
+    fp32_round,
+    mxfp4_quant,
+    pack_nibbles,
+    round_scale,
+    rtn_codes,
+    rtn_quant,
+    unpack_nibbles,
+)

@@ -1,0 +1,249 @@
+"""Pins for the oracle's quantizers, storage rounding and packing (CPU only).
+
+Independent checks: hand-worked golden cases, brute-force nearest-grid-point
+search in exact rational arithmetic (fractions.Fraction) on tiny groups, the
+round-off bounds from the QuIP note ("The math, slowly": per-element error
+within half a step, mean square a twelfth of a step squared), torch's
+float32 -> bfloat16 conversion as a library cross-check for the bfloat16
+rounding, and the MXFP4 scale bracket amax / 2^e in [4, 8).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quant as Q
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+# --------------------------------------------------------------- bf16 / fp32
+
+def test_bf16_round_matches_torch_on_float32_values():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** rng.integers(-20, 20, 200000).astype(np.float32),
+        np.array([1.0, -1.0, 0.0, 3.0e38, 1.1754944e-38], dtype=np.float32),
+    ]).astype(np.float32)
+    v = v[np.isfinite(v)]
+    ours = Q.bf16_round(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_round_ties_to_even():
+    one = 1.0
+    assert Q.bf16_round(one + 2.0 ** -8) == 1.0                       # tie, 1.0 is even
+    assert Q.bf16_round(one + 3 * 2.0 ** -8) == one + 2.0 ** -6       # tie, goes up to even
+    assert Q.bf16_round(one + 2.0 ** -8 + 2.0 ** -30) == one + 2.0 ** -7
+    assert Q.bf16_round(-(one + 2.0 ** -8)) == -1.0
+
+
+def test_bf16_round_direct_from_float64_no_double_rounding():
+    # 1 + 2^-8 - 2^-40 is below the bf16 midpoint; a detour through float32
+    # would round it to 1 + 2^-8 (a tie) first and could then land on the
+    # other side.  Direct rounding gives 1.0.
+    assert Q.bf16_round(1.0 + 2.0 ** -8 - 2.0 ** -40) == 1.0
+    assert Q.bf16_round(1.0 + 3 * 2.0 ** -8 - 2.0 ** -40) == 1.0 + 2.0 ** -7
+
+
+# --------------------------------------------------------------------- RTN
+
+def test_rtn_hand_cases():
+    c = GOLDEN["rtn_sym_g4"]
+    r = oracle.rtn_quant(np.array([c["y"]]), 4, 4, True, "f32")
+    assert r.codes[0].tolist() == c["codes"]
+    assert math.isclose(r.scales[0, 0], c["scale"], rel_tol=1e-7)
+    assert oracle.pack_nibbles(r.codes).tolist() == c["packed_bytes"]
+    c = GOLDEN["rtn_asym_g4"]
+    r = oracle.rtn_quant(np.array([c["y"]]), 4, 4, False, "f32")
+    assert r.codes[0].tolist() == c["codes"]
+    assert r.zeros[0, 0] == c["zero"]
+    assert math.isclose(r.scales[0, 0], c["scale"], rel_tol=1e-7)
+    deq = oracle.dequant_int(r.codes, r.scales, r.zeros, 4)
+    assert np.allclose(deq[0], c["dequant"], rtol=1e-6)
+
+
+def _brute_rtn(vals, bits, sym, scale_dtype):
+    """Nearest grid point by exhaustive search in exact arithmetic."""
+    fr = [Fraction(float(v)) for v in vals]
+    if sym:
+        qmax = (1 << (bits - 1)) - 1
+        amax = max(abs(f) for f in fr)
+        s = float(oracle.round_scale(np.float64(amax / qmax), scale_dtype)) if amax else 0.0
+        s = s if s != 0.0 else 1.0
+        S = Fraction(s)
+        grid = range(-(1 << (bits - 1)), qmax + 1)
+        z = 0
+    else:
+        lo = min(min(fr), Fraction(0))
+        hi = max(max(fr), Fraction(0))
+        levels = (1 << bits) - 1
+        s = float(oracle.round_scale(np.float64((hi - lo) / levels), scale_dtype)) if hi > lo else 0.0
+        s = s if s != 0.0 else 1.0
+        S = Fraction(s)
+        # zero point: nearest integer to -lo / s, ties to even, clamped
+        t = -lo / S
+        z = min(max(_rne_fraction(t), 0), levels)
+        grid = range(0, levels + 1)
+    codes = []
+    for f in fr:
+        best = None
+        for q in grid:
+            d = abs(f - (q - z) * S)
+            key = (d, (q - z) % 2)          # ties: even (q - z)
+            if best is None or key < best[0]:
+                best = (key, q)
+        codes.append(best[1])
+    return codes, s, z
+
+
+def _rne_fraction(t: Fraction) -> int:
+    f = math.floor(t)
+    r = t - f
+    if r > Fraction(1, 2):
+        return f + 1
+    if r < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("scale_dtype", ["f32", "bf16"])
+def test_rtn_brute_force_tiny_groups(sym, scale_dtype):
+    rng = np.random.default_rng(11 if sym else 12)
+    for trial in range(400):
+        g = int(rng.integers(1, 5))
+        kind = trial % 4
+        if kind == 0:
+            vals = rng.standard_normal(g)
+        elif kind == 1:
+            vals = rng.uniform(0.1, 3.0, g)                     # one-signed group
+        elif kind == 2:
+            # values on half-integer multiples of a power-of-two scale: exact ties
+            vals = (rng.integers(-15, 16, g) + 0.5) * 0.25
+            vals[0] = 7 * 0.25 if sym else vals[0]
+        else:
+            vals = rng.standard_normal(g) * 10.0 ** rng.integers(-3, 3)
+        r = oracle.rtn_quant(vals[None, :], g, 4, sym, scale_dtype)
+        codes, s, z = _brute_rtn(vals, 4, sym, scale_dtype)
+        assert r.codes[0].tolist() == codes, (vals, r.codes, codes)
+        assert r.scales[0, 0] == s
+        if not sym:
+            assert r.zeros[0, 0] == z
+
+
+def test_rtn_all_zero_group():
+    r = oracle.rtn_quant(np.zeros((2, 8)), 4, 4, True, "bf16")
+    assert np.all(r.scales == 1.0) and np.all(r.codes == 0)
+    r = oracle.rtn_quant(np.zeros((2, 8)), 4, 4, False, "bf16")
+    assert np.all(r.scales == 1.0) and np.all(r.codes == 0) and np.all(r.zeros == 0)
+
+
+def test_rtn_symmetric_amax_maps_to_full_scale():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((64, 128))
+    r = oracle.rtn_quant(y, 128, 4, True, "bf16")
+    i = np.abs(y).argmax(axis=1)
+    top = r.codes[np.arange(64), i]
+    assert np.all(np.abs(top) == 7)
+    assert r.codes.min() >= -7 and r.codes.max() <= 7
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_rtn_error_bounds(sym):
+    """|y - yhat| <= s/2 for unclamped elements; mean square error close to
+    s^2/12 over many elements (QuIP note, 'The math, slowly')."""
+    rng = np.random.default_rng(4)
+    y = rng.standard_normal((2000, 128))
+    r = oracle.rtn_quant(y, 128, 4, sym, "f32")
+    deq = oracle.dequant_int(r.codes, r.scales, r.zeros, 128)
+    s = np.repeat(r.scales, 128, axis=1)
+    err = (y - deq) / s
+    assert np.all(np.abs(err) <= 0.5 + 1e-9)
+    # interior elements: exclude codes at the ends of the grid
+    q = r.codes
+    interior = (np.abs(q) < 7) if sym else ((q > 0) & (q < 15))
+    e = err[interior]
+    assert e.size > 100000
+    assert abs(np.mean(e * e) - 1.0 / 12.0) < 0.03 / 12.0
+
+
+# ------------------------------------------------------------------- MXFP4
+
+def test_mxfp4_hand_cases():
+    c = GOLDEN["mxfp4_amax5"]
+    y = np.array(c["y"] + [0.0] * (32 - len(c["y"])))
+    r = oracle.mxfp4_quant(y[None, :], 32)
+    assert r.scales[0, 0] == c["e8m0"]
+    assert r.codes[0, :len(c["codes"])].tolist() == c["codes"]
+    deq = oracle.dequant_mxfp4(r.codes, r.scales, 32)[0, :len(c["values"])]
+    assert deq.tolist() == c["values"]
+    assert np.signbit(deq[4])
+    s = GOLDEN["mxfp4_scale"]
+    for amax, e in zip(s["amax"], s["e"]):
+        y = np.zeros(32)
+        y[5] = -amax
+        assert oracle.mxfp4_quant(y[None, :], 32).scales[0, 0] == e + 127
+
+
+def _brute_e2m1(v: float) -> int:
+    """Nearest of the 15 distinct E2M1 values, exact arithmetic, ties to the
+    even mantissa (even index); sign bit kept for negative v."""
+    f = Fraction(float(v))
+    a = abs(f)
+    best = None
+    for idx, val in enumerate(oracle.E2M1_VALUES):
+        d = abs(a - Fraction(float(val)))
+        key = (d, idx % 2)
+        if best is None or key < best[0]:
+            best = (key, idx)
+    return best[1] | (8 if f < 0 else 0)
+
+
+def test_e2m1_brute_force():
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([
+        rng.uniform(-8, 8, 5000),
+        np.arange(-64, 65) / 8.0,            # every multiple of 1/8 in [-8, 8]: all ties
+        [6.0, -6.0, 100.0, -1e9, 0.0, -0.0, 1e-30, -1e-30],
+    ])
+    got = oracle.e2m1_round(vals)
+    exp = np.array([_brute_e2m1(v) for v in vals])
+    assert np.array_equal(got, exp)
+
+
+def test_mxfp4_brute_force_groups():
+    rng = np.random.default_rng(6)
+    for trial in range(60):
+        y = rng.standard_normal(32) * 10.0 ** rng.integers(-6, 6)
+        r = oracle.mxfp4_quant(y[None, :], 32)
+        e = int(r.scales[0, 0]) - 127
+        amax = np.abs(y).max()
+        assert 4.0 <= amax / 2.0 ** e < 8.0
+        # brute force over the 15 distinct values times 2^e
+        for k in range(32):
+            v = Fraction(float(y[k])) / Fraction(2) ** e
+            assert r.codes[0, k] == _brute_e2m1(float(v))
+
+
+def test_mxfp4_zero_group():
+    r = oracle.mxfp4_quant(np.zeros((1, 64)), 32)
+    assert r.scales.tolist() == [[0, 0]] and np.all(r.codes == 0)
+
+
+# ----------------------------------------------------------------- packing
+
+def test_pack_unpack():
+    assert oracle.pack_nibbles([1, 2, 3, 4]).tolist() == [0x21, 0x43]
+    assert oracle.pack_nibbles([-1, 7, -8]).tolist() == [0x7F, 0x08]
+    rng = np.random.default_rng(9)
+    c = rng.integers(-8, 8, 1001)
+    p = oracle.pack_nibbles(c)
+    assert p.size == 501
+    assert np.array_equal(oracle.unpack_nibbles(p, 1001, signed=True), c)
