@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the fused Hadamard rotate + quantize path on one MI355X.
+
+One step is one pass over every stage of the hot path, each on its own
+seeded synthetic input already resident in HBM:
+
+  r1       R1 residual stream: 4096 x 4096 bf16, full FWHT 4096, int4 sym g128
+  r4       R4 down_proj input: 8192 x 14336 bf16, block-diagonal 7 x 2048,
+           int4 asym g128 + uint4 zeros
+  r4_kron  the same input at full width 14336 = 28 x 512 (Kronecker)
+  r3_q     R3 queries 16 x 2048 x 32 x 128 bf16: per-head FWHT 128 -> bf16
+  r3_k     R3 keys (same shape): FWHT 128 + int4 asym per head vector
+  weight   W 14336 x 4096 bf16 -> W.H bf16 + MXFP4 + int4 sym g128, one read
+
+The step touches about 2 GB, eight times the 256 MB Infinity Cache, so every
+launch reads its input from HBM.  Timing uses HIP events on the stream the
+kernels are launched on (torch's current stream).  The value is algorithmic
+bytes (one read of each input plus every mandatory output write) per second
+over the whole step.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
+METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
+PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "hadamard_rotation_preprocessing_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def qbytes(rows, n, spec):
+    groups = rows * n // spec.group_size
+    sb = {"f32": 4, "bf16": 2, "e8m0": 1}[spec.scale_dtype]
+    zb = (groups + 1) // 2 if (spec.format == "int" and not spec.sym) else 0
+    return rows * n // 2 + groups * sb + zb
+
+
+def build_parts(hr, synth, torch, only):
+    """Inputs (CPU and device), launches and algorithmic bytes per kernel."""
+    W = synth.WORKLOADS
+    dev = "cuda:0"
+    parts = {}
+    host = {}
+
+    def want(name):
+        return only is None or name in only
+
+    if want("r1"):
+        w = W["r1"]
+        x = synth.make_inputs(w)
+        spec = hr.QSpec.from_dict(w.qspecs[0])
+        xg = x.to(dev)
+        out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+        parts["r1"] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out),
+                           bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
+        host["r1"] = (x, w.n, 0, [spec], False)
+    if want("r4") or want("r4_kron"):
+        w = W["r4"]
+        x = synth.make_inputs(w)
+        spec = hr.QSpec.from_dict(w.qspecs[0])
+        xg = x.to(dev)
+        b = x.numel() * 2 + qbytes(x.shape[0], w.n, spec)
+        if want("r4"):
+            out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+            parts["r4"] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 2048, spec, out=out),
+                               bytes=b, rows=x.shape[0])
+            host["r4"] = (x, w.n, 2048, [spec], False)
+        if want("r4_kron"):
+            out2 = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+            parts["r4_kron"] = dict(fn=lambda xg=xg, out=out2, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out2),
+                                    bytes=b, rows=x.shape[0])
+            host["r4_kron"] = (x, w.n, 0, [spec], False)
+    if want("r3_q") or want("r3_k"):
+        w = W["r3"]
+        q, k = synth.make_inputs(w)
+        spec = hr.QSpec.from_dict(w.qspecs[0])
+        rows = q.numel() // 128
+        if want("r3_q"):
+            qg = q.to(dev)
+            yq = torch.empty_like(qg)
+            parts["r3_q"] = dict(fn=lambda qg=qg, yq=yq: hr.rotate(qg, 0, out=yq), bytes=q.numel() * 4, rows=rows)
+            host["r3_q"] = (q.reshape(rows, 128), 128, 0, [], True)
+        if want("r3_k"):
+            kg = k.to(dev)
+            out = hr.alloc_quant_outputs(rows, 128, spec, dev)
+            parts["r3_k"] = dict(fn=lambda kg=kg, out=out, spec=spec: hr.rotate_quantize_act(kg, 0, spec, out=out),
+                                 bytes=k.numel() * 2 + qbytes(rows, 128, spec), rows=rows)
+            host["r3_k"] = (k.reshape(rows, 128), 128, 0, [spec], False)
+        del q, k
+    if want("weight"):
+        w = W["weight"]
+        x = synth.make_inputs(w)
+        specs = [hr.QSpec.from_dict(d) for d in w.qspecs]
+        xg = x.to(dev)
+        rows = x.shape[0]
+        out = {"w_rot": torch.empty_like(xg), "quant": [hr.alloc_quant_outputs(rows, w.n, s, dev) for s in specs]}
+        parts["weight"] = dict(fn=lambda xg=xg, out=out, specs=specs: hr.rotate_fuse_weight(xg, 0, specs, out=out),
+                               bytes=x.numel() * 4 + sum(qbytes(rows, w.n, s) for s in specs), rows=rows)
+        host["weight"] = (x, w.n, 0, specs, True)
+    return parts, host
+
+
+def cpu_baseline(host, fraction):
+    """Time the oracle (as it stands) on the first rows of every part: the
+    same fraction of each part's rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    total_bytes = 0
+    t0 = time.perf_counter()
+    for name, (x, n, block, specs, write_rot) in host.items():
+        rows = max(2, int(x.shape[0] * fraction)) // 2 * 2
+        xs = x.reshape(-1, n)[:rows]
+        y = oracle.rotate(xs, n, block)
+        for s in specs:
+            if s.format == "mxfp4":
+                r = oracle.mxfp4_quant(y, 32)
+            else:
+                r = oracle.rtn_quant(y, s.group_size, 4, s.sym, s.scale_dtype)
+            oracle.pack_nibbles(r.codes)
+            if r.zeros is not None:
+                oracle.pack_nibbles(r.zeros)
+        if write_rot:
+            oracle.bf16_round(y)
+        es = 2
+        total_bytes += rows * n * es + (rows * n * es if write_rot else 0) + sum(
+            rows * n // 2 + rows * n // s.group_size * {"f32": 4, "bf16": 2, "e8m0": 1}[s.scale_dtype]
+            + ((rows * n // s.group_size + 1) // 2 if (s.format == "int" and not s.sym) else 0) for s in specs)
+        del y
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "first %.4g of the rows of every part (%d bytes of the step's workload), "
+                      "float64 dense-matrix oracle, %.1f s wall" % (fraction, total_bytes, dt)}
+
+
+def traffic_for(kernel: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("sources_digest") != digest or kernel not in d.get("kernels", {}):
+        return None
+    return d["kernels"][kernel].get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling)" % ",".join(PARTS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path shards rows across GPUs with no communication, "
+              "and this build runs and reports a single MI355X (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hadamard_rotation_preprocessing_amd as hr
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    only = set(args.only.split(",")) if args.only else None
+    t_gen = time.perf_counter()
+    parts, host = build_parts(hr, synth, torch, only)
+    torch.cuda.synchronize()
+    print("inputs ready in %.1f s: %s" % (time.perf_counter() - t_gen, ", ".join(parts)), file=sys.stderr, flush=True)
+    names = [p for p in PARTS if p in parts]
+
+    for _ in range(args.warmup):
+        for nm in names:
+            parts[nm]["fn"]()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for nm in names}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for nm in names:
+            a, b = ev[nm][s]
+            a.record(stream)
+            parts[nm]["fn"]()
+            b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    step_bytes = sum(parts[nm]["bytes"] for nm in names)
+    step_rows = sum(parts[nm]["rows"] for nm in names)
+    per = {}
+    for nm in names:
+        ms = sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps
+        gbs = parts[nm]["bytes"] / (ms * 1e-3) / 1e9
+        per[nm] = {"ms": round(ms, 5), "bytes": parts[nm]["bytes"], "GB_s": round(gbs, 1),
+                   "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_per_s": round(parts[nm]["rows"] / (ms * 1e-3), 1)}
+    dom = max(names, key=lambda nm: per[nm]["ms"])
+    digest = sources_digest()
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": per[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": per[dom]["frac"], "traffic": traffic_for(dom, digest),
+                "algorithmic_bytes_per_launch": parts[dom]["bytes"], "launch_ms": per[dom]["ms"]}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded tensors shaped like 8B-class layers (no real activations or weights)",
+        "config": {"workload": "hot-path step: " + " + ".join(names), "bytes_per_step": step_bytes,
+                   "rows_per_step": step_rows, "io": "bf16 in; int4/MXFP4 codes, bf16 scales/outputs",
+                   "parts": per},
+        "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "sources_digest": digest,
+    }
+    if not args.no_cpu_baseline and only is None:
+        out["cpu_baseline"] = cpu_baseline(host, args.cpu_fraction)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,472 @@
+// C-ABI entry points: argument validation, launch planning, dispatch.
+//
+// Every check runs before anything is enqueued, so a failing call leaves all
+// outputs untouched (the all-or-nothing convention of the AIMET SpinQuant
+// page: validate every pass, then mutate).  No silent fallback exists: a
+// shape the kernels do not cover returns HR_EUNSUPPORTED.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/hadarot.h"
+#include "plan.h"
+
+namespace hr {
+bool paley_matrix(int k, std::vector<int8_t>& h);
+int64_t kron_order(int64_t n);
+}  // namespace hr
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int ok() {
+    g_err.clear();
+    return HR_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+    int l = 0;
+    while ((int64_t{1} << l) < v) ++l;
+    return l;
+}
+
+size_t dtype_size(int dt) { return dt == HR_F32 ? 4 : (dt == HR_BF16 ? 2 : 1); }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Validated quantizer spec.
+struct QSpec {
+    int format, sym, logg, scale_dtype;
+    int64_t g;
+};
+
+int check_qspec(const hr_qspec* q, int64_t n, QSpec* out) {
+    if (!q) return fail(HR_EINVAL, "quantizer spec is NULL");
+    if (q->format != HR_Q_INT && q->format != HR_Q_MXFP4)
+        return fail(HR_EINVAL, "quantizer format %d is not HR_Q_INT or HR_Q_MXFP4", q->format);
+    if (q->bits != 4) return fail(HR_EUNSUPPORTED, "bits = %d: only 4-bit codes are implemented", q->bits);
+    const int64_t g = q->group_size;
+    if (q->format == HR_Q_MXFP4) {
+        if (g != 32) return fail(HR_EINVAL, "MXFP4 requires group_size 32 (got %lld)", (long long)g);
+        if (q->scale_dtype != HR_E8M0) return fail(HR_EINVAL, "MXFP4 requires scale_dtype HR_E8M0");
+    } else {
+        if (g <= 0 || g % 2) return fail(HR_EINVAL, "group_size %lld must be positive and even", (long long)g);
+        if (q->sym != 0 && q->sym != 1) return fail(HR_EINVAL, "sym must be 0 or 1");
+        if (q->scale_dtype != HR_F32 && q->scale_dtype != HR_BF16)
+            return fail(HR_EINVAL, "INT scales must be HR_F32 or HR_BF16");
+    }
+    if (n % g) return fail(HR_EINVAL, "group_size %lld does not divide n = %lld", (long long)g, (long long)n);
+    if (!is_pow2(g)) return fail(HR_EUNSUPPORTED, "group_size %lld is not a power of two", (long long)g);
+    out->format = q->format;
+    out->sym = q->format == HR_Q_INT ? q->sym : 1;
+    out->g = g;
+    out->logg = ilog2(g);
+    out->scale_dtype = q->format == HR_Q_MXFP4 ? 2 : (q->scale_dtype == HR_BF16 ? 1 : 0);
+    return HR_OK;
+}
+
+int check_shape(int dtype, int64_t rows, int64_t n) {
+    if (dtype != HR_F32 && dtype != HR_BF16) return fail(HR_EINVAL, "dtype %d is not HR_F32 or HR_BF16", dtype);
+    if (rows < 0) return fail(HR_EINVAL, "rows = %lld is negative", (long long)rows);
+    if (n <= 0) return fail(HR_EINVAL, "n = %lld must be positive", (long long)n);
+    if (n > (int64_t{1} << 40) || (rows > 0 && rows > (int64_t{1} << 50) / n))
+        return fail(HR_EINVAL, "tensor too large (rows = %lld, n = %lld)", (long long)rows, (long long)n);
+    return HR_OK;
+}
+
+// Rotation geometry: Sylvester block or Kronecker factorisation.
+struct Geometry {
+    int logb;       // log2 of the Hadamard block (Sylvester) or of M (Kronecker)
+    int kron_k;     // 0 or the base order
+    int64_t block;  // B (Sylvester) or M (Kronecker)
+    float norm;
+};
+
+int check_block(int64_t n, int64_t block, Geometry* g) {
+    g->kron_k = 0;
+    if (block > 0 && block != n) {
+        if (!is_pow2(block)) return fail(HR_EINVAL, "block %lld is not a power of two", (long long)block);
+        if (n % block) return fail(HR_EINVAL, "block %lld does not divide n = %lld", (long long)block, (long long)n);
+        if (block > 32768) return fail(HR_EUNSUPPORTED, "block %lld exceeds 32768", (long long)block);
+        g->block = block;
+        g->logb = ilog2(block);
+        g->norm = static_cast<float>(1.0 / sqrt(static_cast<double>(block)));
+        return HR_OK;
+    }
+    if (is_pow2(n)) {
+        if (n > 32768) return fail(HR_EUNSUPPORTED, "full-width rotation of n = %lld exceeds 32768", (long long)n);
+        g->block = n;
+        g->logb = ilog2(n);
+        g->norm = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
+        return HR_OK;
+    }
+    const int64_t k = hr::kron_order(n);
+    if (k == 0) return fail(HR_EUNSUPPORTED, "no supported base Hadamard order for n = %lld", (long long)n);
+    if (k > hr::kMaxKron)
+        return fail(HR_EUNSUPPORTED, "Kronecker base order %lld for n = %lld exceeds %d", (long long)k,
+                    (long long)n, hr::kMaxKron);
+    if (n > 32768) return fail(HR_EUNSUPPORTED, "Kronecker rotation of n = %lld exceeds 32768", (long long)n);
+    g->kron_k = static_cast<int>(k);
+    g->block = n / k;
+    g->logb = ilog2(g->block);
+    g->norm = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
+    return HR_OK;
+}
+
+int check_ptr(const void* p, const char* name, size_t align) {
+    if (!p) return fail(HR_EINVAL, "%s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(p) % align)
+        return fail(HR_EINVAL, "%s is not %zu-byte aligned", name, align);
+    return HR_OK;
+}
+
+// Builds the launch plan (threads per chunk, chunks per workgroup, LDS).
+int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSpec* qs, int nq,
+              hr::RotPlan* p) {
+    memset(p, 0, sizeof *p);
+    p->bf16 = dtype == HR_BF16;
+    int64_t gmin = INT64_MAX, gmax = 1;
+    bool asym_one_group = false;
+    for (int i = 0; i < nq; ++i) {
+        if (qs[i].g < gmin) gmin = qs[i].g;
+        if (qs[i].g > gmax) gmax = qs[i].g;
+    }
+    // chunk: whole Hadamard blocks and whole groups
+    int64_t chunk;
+    if (geo.kron_k) {
+        chunk = n;
+    } else {
+        chunk = geo.block;
+        if (gmax > chunk) chunk = gmax;
+        // small blocks: let one chunk span several blocks so that a thread
+        // still owns 16 contiguous elements
+        while (chunk < 16 && n % (2 * chunk) == 0) chunk *= 2;
+    }
+    // elements per thread: at most 16 (32 when a chunk needs it), at most
+    // the smallest group and the chunk
+    int64_t e = 16;
+    if (chunk / e > 1024) e = 32;
+    if (nq && gmin < e) e = gmin;
+    if (chunk < e) e = chunk;
+    if (e < 2) e = 2;
+    if (chunk % e) return fail(HR_EUNSUPPORTED, "chunk of %lld elements is not a multiple of %lld",
+                                (long long)chunk, (long long)e);
+    const int64_t tpc = chunk / e;
+    if (tpc > 1024)
+        return fail(HR_EUNSUPPORTED, "%lld elements per chunk need more than 1024 threads "
+                    "(group_size %lld too small for this block)", (long long)chunk, (long long)gmin);
+    if (geo.kron_k && e < 8)
+        return fail(HR_EUNSUPPORTED, "Kronecker rotation needs group_size >= 8");
+    int64_t cpw = tpc >= 256 ? 1 : 256 / tpc;
+    for (int i = 0; i < nq; ++i)
+        if (qs[i].format == HR_Q_INT && !qs[i].sym && (cpw * chunk / qs[i].g) % 2) asym_one_group = true;
+    if (asym_one_group) cpw *= 2;  // zero points are packed two groups per byte
+    const int64_t nt = cpw * tpc;
+    if (nt > 1024) return fail(HR_EUNSUPPORTED, "workgroup of %lld threads needed", (long long)nt);
+    const int64_t total_elems = rows * n;
+    const int64_t total_chunks = total_elems / chunk;
+    p->loge = ilog2(e);
+    p->nt = static_cast<int>(nt);
+    p->grid = (total_chunks + cpw - 1) / cpw;
+    if (p->grid > 0x7FFFFFFF) return fail(HR_EUNSUPPORTED, "grid too large");
+    if (geo.kron_k) p->kmax = geo.kron_k <= 16 ? 16 : (geo.kron_k <= 32 ? 32 : 64);
+    const int64_t wg_elems = nt * e;
+    size_t lds = static_cast<size_t>(wg_elems + (wg_elems >> 4)) * 4;  // padded transform buffer
+    lds += static_cast<size_t>(2 * (nt / 64 + 1)) * 4;                  // cross-wave reduction
+    if (nq) lds += static_cast<size_t>(wg_elems / gmin) * 4;           // zero-point staging
+    if (lds > 160 * 1024) return fail(HR_EUNSUPPORTED, "needs %zu bytes of LDS", lds);
+    p->lds_bytes = lds;
+    hr::RotArgs& a = p->a;
+    a.total_chunks = total_chunks;
+    a.norm = geo.norm;
+    a.logb = geo.logb;
+    a.chunk = static_cast<int32_t>(chunk);
+    a.tpc = static_cast<int32_t>(tpc);
+    a.cpw = static_cast<int32_t>(cpw);
+    a.kron_k = geo.kron_k;
+    a.nq = nq;
+    for (int i = 0; i < nq; ++i) {
+        a.total_groups[i] = total_elems / qs[i].g;
+        a.q[i].format = qs[i].format;
+        a.q[i].sym = qs[i].sym;
+        a.q[i].logg = qs[i].logg;
+        a.q[i].scale_dtype = qs[i].scale_dtype;
+    }
+    if (geo.kron_k) {
+        std::vector<int8_t> h;
+        if (!hr::paley_matrix(geo.kron_k, h)) return fail(HR_EUNSUPPORTED, "no base matrix of order %d", geo.kron_k);
+        for (int c = 0; c < geo.kron_k; ++c) {
+            uint64_t m = 0;
+            for (int r = 0; r < geo.kron_k; ++r)
+                if (h[static_cast<size_t>(r) * geo.kron_k + c] < 0) m |= uint64_t{1} << r;
+            a.hk_neg[c] = m;
+        }
+    }
+    return HR_OK;
+}
+
+int run(const hr::RotPlan& p, void* stream) {
+    if (p.grid == 0) return ok();
+    const int e = hr::launch_rotate(p, stream);
+    if (e != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
+    return ok();
+}
+
+struct QBuf {
+    Range codes, scales, zeros;
+};
+
+int check_qbuffers(const QSpec& q, int64_t rows, int64_t n, void* codes, void* scales, void* zeros, const char* tag,
+                   QBuf* b) {
+    char nm[64];
+    snprintf(nm, sizeof nm, "%scodes", tag);
+    int st = check_ptr(codes, nm, 16);
+    if (st) return st;
+    const size_t sal = q.scale_dtype == 0 ? 4 : (q.scale_dtype == 1 ? 2 : 1);
+    snprintf(nm, sizeof nm, "%sscales", tag);
+    st = check_ptr(scales, nm, sal);
+    if (st) return st;
+    const int64_t groups = rows * n / q.g;
+    b->codes = {"codes", reinterpret_cast<uintptr_t>(codes), reinterpret_cast<uintptr_t>(codes) + (size_t)(rows * n / 2)};
+    b->scales = {"scales", reinterpret_cast<uintptr_t>(scales), reinterpret_cast<uintptr_t>(scales) + (size_t)groups * sal};
+    b->zeros = {"zeros", 0, 0};
+    if (q.format == HR_Q_INT && !q.sym) {
+        snprintf(nm, sizeof nm, "%szeros", tag);
+        st = check_ptr(zeros, nm, 1);
+        if (st) return st;
+        b->zeros = {"zeros", reinterpret_cast<uintptr_t>(zeros), reinterpret_cast<uintptr_t>(zeros) + (size_t)((groups + 1) / 2)};
+    } else if (zeros) {
+        return fail(HR_EINVAL, "%szeros must be NULL for a symmetric or MXFP4 quantizer", tag);
+    }
+    return HR_OK;
+}
+
+int check_disjoint(const std::vector<Range>& rs) {
+    for (size_t i = 0; i < rs.size(); ++i)
+        for (size_t j = i + 1; j < rs.size(); ++j)
+            if (rs[i].hi > rs[i].lo && rs[j].hi > rs[j].lo && overlap(rs[i], rs[j]))
+                return fail(HR_EINVAL, "buffers %s and %s overlap", rs[i].name, rs[j].name);
+    return HR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hr_last_error(void) { return g_err.c_str(); }
+
+int hr_kron_order(int64_t n, int32_t* K, int64_t* M, int8_t* hk) {
+    if (n <= 0 || is_pow2(n)) return fail(HR_EINVAL, "n = %lld is not a positive non-power-of-two", (long long)n);
+    const int64_t k = hr::kron_order(n);
+    if (k == 0) return fail(HR_EUNSUPPORTED, "no supported base Hadamard order for n = %lld", (long long)n);
+    if (K) *K = static_cast<int32_t>(k);
+    if (M) *M = n / k;
+    if (hk) {
+        std::vector<int8_t> h;
+        if (!hr::paley_matrix(static_cast<int>(k), h)) return fail(HR_EUNSUPPORTED, "no base matrix");
+        memcpy(hk, h.data(), h.size());
+    }
+    return ok();
+}
+
+int hadamard_rotate(const void* x, void* y, int dtype, int64_t rows, int64_t n, int64_t block, void* stream) {
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    st = check_block(n, block, &geo);
+    if (st) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(x, "x", 16)) || (st = check_ptr(y, "y", 16))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    if (x != y) {
+        Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
+        Range ry{"y", reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(y) + bytes};
+        if (overlap(rx, ry)) return fail(HR_EINVAL, "y partially overlaps x");
+    }
+    hr::RotPlan p;
+    st = make_plan(dtype, rows, n, geo, nullptr, 0, &p);
+    if (st) return st;
+    p.a.x = x;
+    p.a.y_rot = y;
+    return run(p, stream);
+}
+
+int rotate_quantize_act(const void* x, int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q,
+                        void* codes, void* scales, void* zeros, void* y_rot, void* stream) {
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    if ((st = check_block(n, block, &geo))) return st;
+    QSpec qs;
+    if ((st = check_qspec(q, n, &qs))) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(x, "x", 16))) return st;
+    QBuf b;
+    if ((st = check_qbuffers(qs, rows, n, codes, scales, zeros, "", &b))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
+    std::vector<Range> rs{b.codes, b.scales, b.zeros};
+    if (y_rot) {
+        if ((st = check_ptr(y_rot, "y_rot", 16))) return st;
+        Range ry{"y_rot", reinterpret_cast<uintptr_t>(y_rot), reinterpret_cast<uintptr_t>(y_rot) + bytes};
+        if (y_rot != x && overlap(rx, ry)) return fail(HR_EINVAL, "y_rot partially overlaps x");
+        rs.push_back(ry);
+    }
+    if ((st = check_disjoint(rs))) return st;
+    for (const Range& r : std::vector<Range>{b.codes, b.scales, b.zeros})
+        if (r.hi > r.lo && overlap(r, rx)) return fail(HR_EINVAL, "output %s overlaps x", r.name);
+    hr::RotPlan p;
+    if ((st = make_plan(dtype, rows, n, geo, &qs, 1, &p))) return st;
+    p.a.x = x;
+    p.a.y_rot = y_rot;
+    p.a.q[0].codes = static_cast<uint8_t*>(codes);
+    p.a.q[0].scales = scales;
+    p.a.q[0].zeros = static_cast<uint8_t*>(zeros);
+    return run(p, stream);
+}
+
+int rotate_fuse_weight(const void* w, int dtype, int64_t out_features, int64_t in_features, int64_t block,
+                       void* w_rot, const hr_qspec* q, int nq, const hr_qout* outs, void* stream) {
+    const int64_t rows = out_features, n = in_features;
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    if ((st = check_block(n, block, &geo))) return st;
+    if (nq < 0 || nq > hr::kMaxQuant) return fail(HR_EINVAL, "nq = %d must be 0, 1 or 2", nq);
+    if (nq > 0 && (!q || !outs)) return fail(HR_EINVAL, "q and outs must be given when nq > 0");
+    if (nq == 0 && !w_rot) return fail(HR_EINVAL, "nothing to compute: w_rot is NULL and nq = 0");
+    QSpec qs[hr::kMaxQuant];
+    for (int i = 0; i < nq; ++i)
+        if ((st = check_qspec(&q[i], n, &qs[i]))) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(w, "w", 16))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    Range rw{"w", reinterpret_cast<uintptr_t>(w), reinterpret_cast<uintptr_t>(w) + bytes};
+    std::vector<Range> rs;
+    if (w_rot) {
+        if ((st = check_ptr(w_rot, "w_rot", 16))) return st;
+        rs.push_back({"w_rot", reinterpret_cast<uintptr_t>(w_rot), reinterpret_cast<uintptr_t>(w_rot) + bytes});
+    }
+    for (int i = 0; i < nq; ++i) {
+        QBuf b;
+        const char* tag = i == 0 ? "outs[0]." : "outs[1].";
+        if ((st = check_qbuffers(qs[i], rows, n, outs[i].codes, outs[i].scales, outs[i].zeros, tag, &b))) return st;
+        rs.push_back(b.codes);
+        rs.push_back(b.scales);
+        rs.push_back(b.zeros);
+    }
+    if ((st = check_disjoint(rs))) return st;
+    for (const Range& r : rs)
+        if (r.hi > r.lo && overlap(r, rw)) return fail(HR_EINVAL, "output %s overlaps w", r.name);
+    hr::RotPlan p;
+    if ((st = make_plan(dtype, rows, n, geo, qs, nq, &p))) return st;
+    p.a.x = w;
+    p.a.y_rot = w_rot;
+    for (int i = 0; i < nq; ++i) {
+        p.a.q[i].codes = static_cast<uint8_t*>(outs[i].codes);
+        p.a.q[i].scales = outs[i].scales;
+        p.a.q[i].zeros = static_cast<uint8_t*>(outs[i].zeros);
+    }
+    return run(p, stream);
+}
+
+int dequant_check(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
+                  int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* stream) {
+    int st = check_shape(HR_F32, rows, n);
+    if (st) return st;
+    QSpec qs;
+    if ((st = check_qspec(q, n, &qs))) return st;
+    if (!deq && !stats) return fail(HR_EINVAL, "nothing to compute: deq and stats are NULL");
+    if (stats && !ref) return fail(HR_EINVAL, "stats requires ref");
+    if (ref && ref_dtype != HR_F32 && ref_dtype != HR_BF16) return fail(HR_EINVAL, "ref_dtype must be HR_F32 or HR_BF16");
+    if (rows == 0) {
+        if (stats) memset(stats, 0, sizeof *stats);
+        return ok();
+    }
+    QBuf b;
+    if ((st = check_qbuffers(qs, rows, n, const_cast<void*>(codes), const_cast<void*>(scales),
+                             const_cast<void*>(zeros), "", &b)))
+        return st;
+    std::vector<Range> ins{b.codes, b.scales, b.zeros};
+    if (ref) {
+        if ((st = check_ptr(ref, "ref", 16))) return st;
+        ins.push_back({"ref", reinterpret_cast<uintptr_t>(ref),
+                       reinterpret_cast<uintptr_t>(ref) + (size_t)(rows * n) * dtype_size(ref_dtype)});
+    }
+    if (deq) {
+        if ((st = check_ptr(deq, "deq", 16))) return st;
+        Range rd{"deq", reinterpret_cast<uintptr_t>(deq), reinterpret_cast<uintptr_t>(deq) + (size_t)(rows * n) * 4};
+        for (const Range& r : ins)
+            if (r.hi > r.lo && overlap(r, rd)) return fail(HR_EINVAL, "deq overlaps %s", r.name);
+    }
+    hr::DqArgs a{};
+    a.codes = static_cast<const uint8_t*>(codes);
+    a.scales = scales;
+    a.zeros = static_cast<const uint8_t*>(zeros);
+    a.ref = stats ? ref : nullptr;
+    a.deq = deq;
+    a.total = rows * n;
+    a.format = qs.format;
+    a.sym = qs.sym;
+    a.logg = qs.logg;
+    a.scale_dtype = qs.scale_dtype;
+    a.ref_bf16 = ref_dtype == HR_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hr::DqAccum* acc = nullptr;
+    if (stats) {
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&acc), sizeof(hr::DqAccum));
+        if (e != hipSuccess) return fail(HR_EDEVICE, "hipMalloc failed: %s", hipGetErrorString(e));
+        e = hipMemsetAsync(acc, 0, sizeof(hr::DqAccum), s);
+        if (e != hipSuccess) {
+            (void)hipFree(acc);
+            return fail(HR_EDEVICE, "hipMemsetAsync failed: %s", hipGetErrorString(e));
+        }
+        a.stats = acc;
+    }
+    const int le = hr::launch_dequant(a, stream);
+    if (le != 0) {
+        if (acc) (void)hipFree(acc);
+        return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(le)));
+    }
+    if (stats) {
+        hr::DqAccum h;
+        hipError_t e = hipMemcpyAsync(&h, acc, sizeof h, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        (void)hipFree(acc);
+        if (e != hipSuccess) return fail(HR_EDEVICE, "reading statistics failed: %s", hipGetErrorString(e));
+        float mx;
+        memcpy(&mx, &h.max_err_bits, sizeof mx);
+        stats->max_err_steps = mx;
+        stats->n_over_half_step = static_cast<int64_t>(h.n_over);
+        stats->n_clamped = static_cast<int64_t>(h.n_clamped);
+        stats->rel_l2_err = h.sum_ref2 > 0 ? sqrt(h.sum_err2 / h.sum_ref2) : 0.0;
+    }
+    return ok();
+}
+
+}  // extern "C"

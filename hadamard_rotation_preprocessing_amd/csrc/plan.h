@@ -1,0 +1,78 @@
+// Launch plan and kernel argument structs shared by the host dispatcher and
+// the kernels.  Plain data only.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hr {
+
+constexpr int kMaxQuant = 2;
+constexpr int kMaxKron = 64;   // largest Kronecker base order handled on the GPU
+
+// One quantizer epilogue, resolved to device pointers.
+struct QuantDev {
+    int32_t format;       // 0 INT, 1 MXFP4
+    int32_t sym;          // INT: 1 symmetric, 0 asymmetric
+    int32_t logg;         // log2(group_size)
+    int32_t scale_dtype;  // 0 f32, 1 bf16, 2 e8m0
+    uint8_t* codes;
+    void* scales;
+    uint8_t* zeros;       // INT asymmetric only
+};
+
+// Arguments of the rotate(+quantize) kernel family.
+struct RotArgs {
+    const void* x;
+    void* y_rot;              // nullable: rotated output in the input dtype
+    int64_t total_chunks;     // chunks in the flattened tensor
+    int64_t total_groups[kMaxQuant];
+    float norm;               // 1/sqrt(block) or 1/sqrt(n) (Kronecker)
+    int32_t logb;             // Hadamard block (Sylvester) or M (Kronecker) bits
+    int32_t chunk;            // elements per chunk (C)
+    int32_t tpc;              // threads per chunk (C / E)
+    int32_t cpw;              // chunks per workgroup
+    int32_t kron_k;           // 0: none; else the base order K (C = K * 2^logb)
+    int32_t nq;
+    QuantDev q[kMaxQuant];
+    // Kronecker base matrix, by output column c: bit a of hk_neg[c] set iff
+    // H_K[a][c] == -1, so that y_c = sum_a H_K[a][c] z_a (y = H_K^T z).
+    uint64_t hk_neg[kMaxKron];
+};
+
+// Host-side plan.
+struct RotPlan {
+    int bf16;        // input/output dtype is bfloat16
+    int loge;        // log2 elements per thread
+    int kmax;        // 0, 16, 32, 64: register bound for the Kronecker mix
+    int nt;          // threads per workgroup
+    int64_t grid;    // workgroups
+    size_t lds_bytes;
+    RotArgs a;
+};
+
+struct DqArgs {
+    const uint8_t* codes;
+    const void* scales;
+    const uint8_t* zeros;
+    const void* ref;       // nullable
+    float* deq;            // nullable
+    void* stats;           // nullable: DqAccum on the device
+    int64_t total;         // elements
+    int32_t format, sym, logg, scale_dtype, ref_bf16;
+};
+
+// Device accumulators of dequant_check.
+struct DqAccum {
+    double sum_err2;
+    double sum_ref2;
+    unsigned long long n_over;
+    unsigned long long n_clamped;
+    unsigned int max_err_bits;   // non-negative float as bits (monotone)
+    unsigned int pad;
+};
+
+int launch_rotate(const RotPlan& p, void* stream);        // returns hipError_t
+int launch_dequant(const DqArgs& a, void* stream);        // returns hipError_t
+
+}  // namespace hr

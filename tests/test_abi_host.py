@@ -1,0 +1,147 @@
+"""CPU tests of the C ABI (no GPU): the library loads, exports every symbol
+declared in include/hadarot.h, and rejects every invalid argument with the
+documented status before anything touches the device.  Pointers here are
+fake, aligned addresses: every case fails validation, so nothing is
+dereferenced and no HIP call is made."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from hadamard_rotation_preprocessing_amd import _lib as L
+from hadamard_rotation_preprocessing_amd import kron_order
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+P = 0x7F0000000000           # fake 16-byte-aligned device addresses, far apart
+A, B, C, D, Z = (ctypes.c_void_p(P + i * (1 << 36)) for i in range(5))
+NUL = None
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hadarot.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_header_symbol():
+    lib = L.lib()
+    names = header_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def q(fmt=L.HR_Q_INT, bits=4, g=128, sym=1, sd=L.HR_BF16):
+    return ctypes.byref(L.hr_qspec(fmt, bits, g, sym, sd))
+
+
+def rqa(x=A, dt=L.HR_BF16, rows=16, n=4096, block=0, qs=None, codes=B, scales=C, zeros=NUL, yrot=NUL):
+    return L.lib().rotate_quantize_act(x, dt, rows, n, block, qs if qs is not None else q(),
+                                       codes, scales, zeros, yrot, None)
+
+
+def msg():
+    return L.lib().hr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dt=7), L.HR_EINVAL, "dtype"),
+    (dict(rows=-1), L.HR_EINVAL, "rows"),
+    (dict(n=0), L.HR_EINVAL, "n = 0"),
+    (dict(block=3), L.HR_EINVAL, "power of two"),
+    (dict(n=4096, block=8192), L.HR_EINVAL, "does not divide"),
+    (dict(qs=q(bits=3)), L.HR_EUNSUPPORTED, "bits"),
+    (dict(qs=q(g=0)), L.HR_EINVAL, "group_size"),
+    (dict(qs=q(g=7)), L.HR_EINVAL, "even"),
+    (dict(n=4096, qs=q(g=96)), L.HR_EINVAL, "divide"),
+    (dict(n=96 * 64, block=32, qs=q(g=96)), L.HR_EUNSUPPORTED, "power of two"),
+    (dict(qs=q(sym=2)), L.HR_EINVAL, "sym"),
+    (dict(qs=q(sd=L.HR_E8M0)), L.HR_EINVAL, "INT scales"),
+    (dict(qs=q(fmt=L.HR_Q_MXFP4, g=64, sd=L.HR_E8M0)), L.HR_EINVAL, "32"),
+    (dict(qs=q(fmt=L.HR_Q_MXFP4, g=32, sd=L.HR_BF16)), L.HR_EINVAL, "E8M0"),
+    (dict(qs=q(fmt=5)), L.HR_EINVAL, "format"),
+    (dict(x=NUL), L.HR_EINVAL, "x is NULL"),
+    (dict(x=ctypes.c_void_p(P + 8)), L.HR_EINVAL, "aligned"),
+    (dict(codes=NUL), L.HR_EINVAL, "codes is NULL"),
+    (dict(codes=ctypes.c_void_p(P + (1 << 36) + 4)), L.HR_EINVAL, "aligned"),
+    (dict(scales=ctypes.c_void_p(P + 2 * (1 << 36) + 1)), L.HR_EINVAL, "aligned"),
+    (dict(qs=q(sym=0), zeros=NUL), L.HR_EINVAL, "zeros is NULL"),
+    (dict(zeros=D), L.HR_EINVAL, "must be NULL"),
+    (dict(codes=ctypes.c_void_p(P + 1024)), L.HR_EINVAL, "overlaps x"),
+    (dict(scales=ctypes.c_void_p(P + (1 << 36) + 64)), L.HR_EINVAL, "overlap"),
+    (dict(yrot=ctypes.c_void_p(P + 4096)), L.HR_EINVAL, "partially overlaps"),
+    (dict(n=4097 * 2, block=0, qs=q(g=2)), L.HR_EUNSUPPORTED, "base Hadamard"),
+    (dict(n=65536, block=0), L.HR_EUNSUPPORTED, "exceeds"),
+    (dict(n=131072, block=65536), L.HR_EUNSUPPORTED, "exceeds 32768"),
+    (dict(n=4096, block=4096, qs=q(g=2)), L.HR_EUNSUPPORTED, "1024 threads"),
+    (dict(n=128 * 108, block=0), L.HR_EUNSUPPORTED, "exceeds 64"),
+])
+def test_rotate_quantize_act_validation(kw, status, text):
+    st = rqa(**kw)
+    assert st == status, (st, msg())
+    assert text in msg(), msg()
+
+
+def test_empty_tensor_is_ok_without_device():
+    assert rqa(rows=0, x=NUL, codes=NUL, scales=NUL) == L.HR_OK
+    assert L.lib().hadamard_rotate(None, None, L.HR_BF16, 0, 128, 0, None) == L.HR_OK
+    assert msg() == ""
+
+
+def test_hadamard_rotate_validation():
+    lib = L.lib()
+    assert lib.hadamard_rotate(A, ctypes.c_void_p(P + 16), L.HR_F32, 4, 128, 0, None) == L.HR_EINVAL
+    assert "partially overlaps" in msg()
+    assert lib.hadamard_rotate(A, B, L.HR_F32, 4, 100, 0, None) == L.HR_EUNSUPPORTED   # 100 = 25 * 4: no order
+    assert lib.hadamard_rotate(A, B, L.HR_F32, 4, 128, 6, None) == L.HR_EINVAL
+    assert lib.hadamard_rotate(NUL, B, L.HR_F32, 4, 128, 0, None) == L.HR_EINVAL
+
+
+def test_rotate_fuse_weight_validation():
+    lib = L.lib()
+    specs = (L.hr_qspec * 3)(L.hr_qspec(1, 4, 32, 1, 2), L.hr_qspec(0, 4, 128, 1, 1), L.hr_qspec(0, 4, 128, 1, 1))
+    outs = (L.hr_qout * 3)(L.hr_qout(B.value, C.value, None), L.hr_qout(D.value, Z.value, None),
+                           L.hr_qout(D.value, Z.value, None))
+    assert lib.rotate_fuse_weight(A, L.HR_BF16, 64, 4096, 0, None, specs, 0, outs, None) == L.HR_EINVAL
+    assert "nothing to compute" in msg()
+    assert lib.rotate_fuse_weight(A, L.HR_BF16, 64, 4096, 0, None, specs, 3, outs, None) == L.HR_EINVAL
+    assert lib.rotate_fuse_weight(A, L.HR_BF16, 64, 4096, 0, None, None, 1, outs, None) == L.HR_EINVAL
+    # two quantizers writing the same codes buffer
+    outs2 = (L.hr_qout * 2)(L.hr_qout(B.value, C.value, None), L.hr_qout(B.value, D.value, None))
+    assert lib.rotate_fuse_weight(A, L.HR_BF16, 64, 4096, 0, None, specs, 2, outs2, None) == L.HR_EINVAL
+    assert "overlap" in msg()
+    # w_rot aliasing w is not allowed for the weight pass
+    assert lib.rotate_fuse_weight(A, L.HR_BF16, 64, 4096, 0, A, specs, 1, outs, None) == L.HR_EINVAL
+
+
+def test_dequant_check_validation():
+    lib = L.lib()
+    st = L.hr_dq_stats()
+    spec = q(sym=1)
+    assert lib.dequant_check(B, C, None, spec, 4, 4096, None, L.HR_F32, None, None, None) == L.HR_EINVAL
+    assert "nothing to compute" in msg()
+    assert lib.dequant_check(B, C, None, spec, 4, 4096, None, L.HR_F32, None, ctypes.byref(st), None) == L.HR_EINVAL
+    assert "requires ref" in msg()
+    assert lib.dequant_check(B, C, None, spec, 4, 4096, A, 9, None, ctypes.byref(st), None) == L.HR_EINVAL
+    assert lib.dequant_check(B, C, None, spec, 4, 4096, A, L.HR_F32, ctypes.c_void_p(P + 64), None, None) == L.HR_EINVAL
+    assert "deq overlaps" in msg()
+
+
+@pytest.mark.parametrize("n", [14336, 96, 5120, 12, 20 * 32, 60 * 8])
+def test_kron_order_matches_oracle_factorisation(n):
+    """The library's base matrix (its own Paley construction in C++) equals the
+    oracle's (built independently in Python) and both factorisations agree."""
+    k, m, h = kron_order(n, with_matrix=True)
+    assert (k, m) == oracle.kron_factor(n)
+    assert np.array_equal(h.astype(np.int64), oracle.paley_hadamard(k))
+
+
+def test_kron_order_errors():
+    lib = L.lib()
+    K, M = ctypes.c_int32(), ctypes.c_int64()
+    assert lib.hr_kron_order(4096, ctypes.byref(K), ctypes.byref(M), None) == L.HR_EINVAL
+    assert lib.hr_kron_order(18, ctypes.byref(K), ctypes.byref(M), None) == L.HR_EUNSUPPORTED

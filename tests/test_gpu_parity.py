@@ -1,0 +1,291 @@
+"""GPU parity: every C-ABI entry point against the oracle on seeded inputs.
+
+Sizes are chosen so that the oracle finishes in seconds while the launches
+still span many workgroups and a ragged tail (a row count that leaves the
+last workgroup partly empty).  Tolerances are those of tests/parity.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import hadamard_rotation_preprocessing_amd as hr
+from parity import Report, check_int, check_mxfp4, check_rotated, to_np64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    hr.lib()
+
+
+def dtname(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def run_act(x, n, block, spec, y_rot=False, ref_y=None):
+    """Rotate+quantize x (CPU tensor [..., n]) on the GPU and check it."""
+    say("rotate_quantize_act", tuple(x.shape), x.dtype, "block", block, spec)
+    xg = x.to(DEV)
+    out = hr.rotate_quantize_act(xg, block, spec, y_rot=y_rot)
+    torch.cuda.synchronize()
+    y = oracle.rotate(x, n, block).reshape(-1, n) if ref_y is None else ref_y
+    kk = oracle.kron_factor(n)[0] if (block <= 0 and n & (n - 1)) else 0
+    rep = Report()
+    if y_rot:
+        check_rotated(to_np64(out["y_rot"]).reshape(-1, n), y, dtname(x), rep)
+    if spec.format == "mxfp4":
+        check_mxfp4(out, y, rep, kron_k=kk)
+    else:
+        check_int(out, y, spec.group_size, spec.sym, spec.scale_dtype, rep, kron_k=kk)
+    say("  ", rep)
+    return out, rep
+
+
+# ------------------------------------------------------------ named workloads
+
+def test_tiny_workload():
+    w = synth.WORKLOADS["tiny"]
+    x = synth.make_inputs(w)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+
+
+def test_r1_reduced_rows():
+    w = synth.WORKLOADS["r1"]
+    x = synth.make_inputs(w, tokens=67)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+
+
+def test_r4_reduced_rows():
+    w = synth.WORKLOADS["r4"]
+    x = synth.make_inputs(w, tokens=37)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+
+
+def test_r4_kronecker_reduced_rows():
+    w = synth.WORKLOADS["r4_kron"]
+    x = synth.make_inputs(w, tokens=13)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+
+
+def test_r3_reduced_query_key():
+    w = synth.WORKLOADS["r3"]
+    q, k = synth.make_inputs(w, batch=1, seq=75)
+    say("hadamard_rotate Q", tuple(q.shape))
+    qg = q.to(DEV)
+    yq = hr.rotate(qg, 0)
+    torch.cuda.synchronize()
+    check_rotated(to_np64(yq).reshape(-1, 128), oracle.rotate(q, 128).reshape(-1, 128), "bf16")
+    run_act(k, 128, 0, hr.QSpec.from_dict(w.qspecs[0]))
+
+
+def test_weight_reduced_rows():
+    w = synth.WORKLOADS["weight"]
+    W = synth.make_inputs(w, out_features=300)
+    specs = [hr.QSpec.from_dict(d) for d in w.qspecs]
+    say("rotate_fuse_weight", tuple(W.shape), specs)
+    out = hr.rotate_fuse_weight(W.to(DEV), 0, specs, w_rot=True)
+    torch.cuda.synchronize()
+    y = oracle.rotate(W, 4096)
+    rep = Report()
+    check_rotated(to_np64(out["w_rot"]), y, "bf16", rep)
+    check_mxfp4(out["quant"][0], y, rep)
+    check_int(out["quant"][1], y, 128, True, "bf16", rep)
+    say("  ", rep)
+
+
+# ------------------------------------------------------------------- sweeps
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("logn", list(range(1, 16)))
+def test_full_width_pow2_rotate(dtype, logn):
+    n = 1 << logn
+    rows = max(3, min(515, (1 << 18) // n)) | 1      # odd row count: ragged tail
+    x = synth.gaussian((rows, n), seed=1000 + logn, dtype=dtype)
+    say("hadamard_rotate", rows, n, dtype)
+    y = hr.rotate(x.to(DEV), 0)
+    torch.cuda.synchronize()
+    check_rotated(to_np64(y), oracle.rotate(x, n), dtname(x))
+
+
+@pytest.mark.parametrize("block", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096])
+def test_block_diagonal_rotate_quant(block):
+    n = 4096
+    x = synth.gaussian((33, n), seed=2000 + block, dtype=torch.bfloat16)
+    run_act(x, n, block, hr.QSpec("int", 4, 128, False, "bf16"), y_rot=True)
+
+
+@pytest.mark.parametrize("g", [2, 4, 8, 16, 32, 64, 128, 256, 512, 2048, 8192])
+@pytest.mark.parametrize("sym", [True, False])
+def test_group_sizes(g, sym):
+    n = 8192
+    x = synth.gaussian((21, n), seed=3000 + g, dtype=torch.float32)
+    block = 2048 if g <= 2048 else 0
+    if g <= 4:
+        block = 1024      # keeps the chunk within 1024 threads
+    run_act(x, n, block, hr.QSpec("int", 4, g, sym, "f32"), y_rot=True)
+
+
+@pytest.mark.parametrize("n", [96, 12 * 256, 20 * 64, 28 * 512, 60 * 64, 44 * 32, 28 * 8])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kronecker_widths(n, dtype):
+    x = synth.gaussian((19, n), seed=4000 + n, dtype=dtype)
+    say("hadamard_rotate (Kronecker)", 19, n, dtype)
+    y = hr.rotate(x.to(DEV), 0)
+    torch.cuda.synchronize()
+    check_rotated(to_np64(y), oracle.rotate(x, n), dtname(x))
+    run_act(x, n, 0, hr.QSpec("int", 4, 32, True, "bf16"), y_rot=True)
+
+
+@pytest.mark.parametrize("rows", [1, 31, 32, 33, 1001])
+def test_head_dim_rows_ragged_asym(rows):
+    # n = 128 with one group per row: zero points pack two rows per byte and an
+    # odd total leaves a padded high nibble
+    x = synth.gaussian((rows, 128), seed=5000 + rows, dtype=torch.bfloat16)
+    out, _ = run_act(x, 128, 0, hr.QSpec("int", 4, 128, False, "bf16"))
+    if rows % 2:
+        assert int(out["zeros"][-1].item()) >> 4 == 0
+
+
+@pytest.mark.parametrize("block", [32, 0])
+def test_mxfp4_activations(block):
+    # block-32 rotation with MXFP4 activations (the pages' accuracy setting)
+    w = synth.WORKLOADS["r1"]
+    x = synth.make_inputs(w, tokens=45)
+    run_act(x, 4096, block, hr.QSpec.mxfp4(), y_rot=True)
+
+
+# ------------------------------------------------------------- special cases
+
+def test_in_place_rotation():
+    x = synth.gaussian((65, 2048), seed=6, dtype=torch.bfloat16)
+    ref = oracle.rotate(x, 2048, 256)
+    xg = x.to(DEV)
+    y = hr.rotate(xg, 256, out=xg)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xg.data_ptr()
+    check_rotated(to_np64(xg), ref, "bf16")
+
+
+def test_in_place_y_rot():
+    x = synth.gaussian((40, 4096), seed=7, dtype=torch.float32)
+    xg = x.to(DEV)
+    spec = hr.QSpec("int", 4, 64, True, "f32")
+    o = hr.alloc_quant_outputs(40, 4096, spec, DEV)
+    o["y_rot"] = xg
+    hr.rotate_quantize_act(xg, 0, spec, y_rot=True, out=o)
+    torch.cuda.synchronize()
+    y = oracle.rotate(x, 4096)
+    check_rotated(to_np64(xg), y, "f32")
+    check_int(o, y, 64, True, "f32", Report())
+
+
+def test_degenerate_groups_and_magnitudes():
+    n = 1024
+    x = synth.gaussian((12, n), seed=8, dtype=torch.float32)
+    x[0] = 0.0                      # all-zero row: scale 1, codes 0
+    x[1] = 3.0                      # constant row: rotation is a single spike
+    x[2] *= 1e-20
+    x[3] *= 1e20
+    x[4] = 0.0
+    x[4, 17] = 5.0                  # one-hot
+    x[5, :512] = 0.0
+    for sym in (True, False):
+        for sd in ("f32", "bf16"):
+            out, _ = run_act(x, n, 0, hr.QSpec("int", 4, 32, sym, sd), y_rot=True)
+            s = to_np64(out["scales"])
+            assert np.all(s[0] == 1.0)
+    out, _ = run_act(x, n, 0, hr.QSpec.mxfp4())
+    assert np.all(out["scales"][0].cpu().numpy() == 0)
+
+
+def test_empty_tensor():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    y = hr.rotate(x, 0)
+    assert y.shape == (0, 256)
+    o = hr.rotate_quantize_act(x, 0, hr.QSpec("int", 4, 128, False, "bf16"))
+    assert o["codes"].shape == (0, 128)
+
+
+def test_errors_leave_outputs_untouched():
+    n = 4096
+    x = synth.gaussian((8, n), seed=9, dtype=torch.bfloat16).to(DEV)
+    spec = hr.QSpec("int", 4, 128, True, "bf16")
+    o = hr.alloc_quant_outputs(8, n, spec, DEV)
+    o["codes"].fill_(0xA5)
+    o["scales"].fill_(-7.0)
+    with pytest.raises(hr.HadarotError):
+        hr.rotate_quantize_act(x, 3, spec, out=o)           # block 3: not a power of two
+    with pytest.raises(hr.HadarotError):
+        hr.rotate_quantize_act(x, 0, hr.QSpec("int", 3, 128, True, "bf16"), out=o)
+    torch.cuda.synchronize()
+    assert bool((o["codes"] == 0xA5).all())
+    assert bool((o["scales"] == -7.0).all())
+
+
+def test_guard_bytes_around_outputs():
+    """Outputs carved from larger buffers: the bytes just before and after
+    each output keep their sentinel value (no out-of-bounds writes)."""
+    rows, n = 37, 2048
+    x = synth.gaussian((rows, n), seed=10, dtype=torch.bfloat16).to(DEV)
+    spec = hr.QSpec("int", 4, 128, False, "bf16")
+    pad = 256
+    cbuf = torch.full((rows * n // 2 + 2 * pad,), 0x5A, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((rows * n // 128 + 2 * pad,), 1234.0, dtype=torch.bfloat16, device=DEV)
+    zbuf = torch.full(((rows * n // 128 + 1) // 2 + 2 * pad,), 0x5A, dtype=torch.uint8, device=DEV)
+    ybuf = torch.full((rows * n + 2 * pad,), 99.0, dtype=torch.bfloat16, device=DEV)
+    o = {"codes": cbuf[pad:-pad].view(rows, n // 2), "scales": sbuf[pad:-pad].view(rows, n // 128),
+         "zeros": zbuf[pad:-pad], "y_rot": ybuf[pad:-pad].view(rows, n)}
+    hr.rotate_quantize_act(x, 512, spec, y_rot=True, out=o)
+    torch.cuda.synchronize()
+    for buf, val in ((cbuf, 0x5A), (zbuf, 0x5A), (sbuf, 1234.0), (ybuf, 99.0)):
+        assert bool((buf[:pad] == val).all()) and bool((buf[-pad:] == val).all())
+    y = oracle.rotate(x.cpu(), n, 512)
+    check_int(o, y, 128, False, "bf16", Report())
+
+
+# ------------------------------------------------------------ dequant_check
+
+@pytest.mark.parametrize("spec", [hr.QSpec("int", 4, 128, True, "bf16"), hr.QSpec("int", 4, 64, False, "f32"),
+                                  hr.QSpec.mxfp4()], ids=["sym-bf16", "asym-f32", "mxfp4"])
+def test_dequant_check(spec):
+    rows, n = 50, 4096
+    x = synth.gaussian((rows, n), seed=11, dtype=torch.bfloat16)
+    out = hr.rotate_quantize_act(x.to(DEV), 0, spec, y_rot=True)
+    deq, st = hr.dequant_check(out, spec, rows, n, ref=out["y_rot"])
+    torch.cuda.synchronize()
+    # the oracle dequantizes the GPU's own codes and scales
+    if spec.format == "mxfp4":
+        codes = oracle.unpack_nibbles(out["codes"].cpu().numpy().reshape(-1), rows * n).reshape(rows, n)
+        ref_deq = oracle.dequant_mxfp4(codes, out["scales"].cpu().numpy().astype(np.int64), 32)
+    else:
+        codes = oracle.unpack_nibbles(out["codes"].cpu().numpy().reshape(-1), rows * n,
+                                      signed=spec.sym).reshape(rows, n)
+        zeros = None
+        if not spec.sym:
+            zeros = oracle.unpack_nibbles(out["zeros"].cpu().numpy(), rows * n // spec.group_size)
+            zeros = zeros.reshape(rows, n // spec.group_size)
+        ref_deq = oracle.dequant_int(codes, to_np64(out["scales"]), zeros, spec.group_size)
+    got = to_np64(deq)
+    assert np.allclose(got, ref_deq, rtol=2.0 ** -23, atol=0)
+    r = to_np64(out["y_rot"])
+    rel = np.linalg.norm(r - ref_deq) / np.linalg.norm(r)
+    assert abs(st["rel_l2_err"] - rel) <= 1e-6 + 1e-4 * rel
+    assert st["max_err_steps"] >= 0
+    if spec.format == "int":
+        # nearest rounding of values inside the grid: within half a step, up
+        # to the bf16 rounding of the reference (2^-8 relative on values of
+        # at most 16 steps)
+        assert st["max_err_steps"] < 0.5 + 16 * 2.0 ** -8
