@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -230,8 +231,38 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     return HR_OK;
 }
 
+// Specialised bf16 kernels (one wave per 128-, 2048- or 4096-element block)
+// take the call when one is compiled for its exact shape; the generic kernel
+// runs otherwise, or always when HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
+    const hr::RotArgs& a = p.a;
+    const char* force = getenv("HADAROT_FORCE_GENERIC");
+    const bool generic_only = force && force[0] == '1';
+    if (!generic_only && p.bf16 && a.kron_k == 0 && (a.logb == 7 || a.logb == 11 || a.logb == 12) &&
+        a.chunk == (1 << a.logb)) {
+        hr::FastKey k{};
+        hr::FastArgs f{};
+        k.logb = a.logb;
+        k.wrot = a.y_rot != nullptr;
+        k.nq = a.nq;
+        for (int i = 0; i < a.nq; ++i) {
+            k.fmt[i] = a.q[i].format;
+            k.sym[i] = a.q[i].sym;
+            k.logg[i] = a.q[i].logg;
+            k.sdt[i] = a.q[i].scale_dtype;
+            f.q[i] = a.q[i];
+            f.total_groups[i] = a.total_groups[i];
+        }
+        f.x = a.x;
+        f.y_rot = a.y_rot;
+        f.units = a.total_chunks;
+        f.norm = a.norm;
+        const int r = hr::launch_fast(k, f, stream);
+        if (r == 1) return ok();
+        if (r < 0)
+            return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));
+    }
     const int e = hr::launch_rotate(p, stream);
     if (e != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
     return ok();

@@ -72,7 +72,28 @@ struct DqAccum {
     unsigned int pad;
 };
 
+// Arguments of the specialised bfloat16 kernels (one wave per block).
+struct FastArgs {
+    const void* x;
+    void* y_rot;              // nullable
+    int64_t units;            // blocks (one wave each) or rows (128-wide kernel)
+    int64_t total_groups[kMaxQuant];
+    float norm;               // 1/sqrt(block)
+    QuantDev q[kMaxQuant];
+};
+
+// Compile-time shape of a specialised kernel, matched at dispatch.
+struct FastKey {
+    int logb;                 // 7, 11 or 12
+    int wrot;                 // rotated output written
+    int nq;
+    int fmt[kMaxQuant], sym[kMaxQuant], logg[kMaxQuant], sdt[kMaxQuant];
+};
+
 int launch_rotate(const RotPlan& p, void* stream);        // returns hipError_t
+// Launches a specialised kernel if one matches `k`: returns 1 if launched,
+// 0 if none matches, or a negative hipError_t on a launch error.
+int launch_fast(const FastKey& k, const FastArgs& a, void* stream);
 int launch_dequant(const DqArgs& a, void* stream);        // returns hipError_t
 
 }  // namespace hr

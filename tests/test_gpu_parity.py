@@ -31,6 +31,17 @@ def gpu_ready():
     hr.lib()
 
 
+@pytest.fixture(params=["fast", "generic"])
+def kernel_path(request, monkeypatch):
+    """Run a test through the specialised bf16 kernels (default dispatch) and
+    again with the generic kernel forced."""
+    if request.param == "generic":
+        monkeypatch.setenv("HADAROT_FORCE_GENERIC", "1")
+    else:
+        monkeypatch.delenv("HADAROT_FORCE_GENERIC", raising=False)
+    return request.param
+
+
 def dtname(t):
     return "bf16" if t.dtype == torch.bfloat16 else "f32"
 
@@ -62,16 +73,18 @@ def test_tiny_workload():
     run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
 
 
-def test_r1_reduced_rows():
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_r1_reduced_rows(kernel_path, y_rot):
     w = synth.WORKLOADS["r1"]
     x = synth.make_inputs(w, tokens=67)
-    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
 
 
-def test_r4_reduced_rows():
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_r4_reduced_rows(kernel_path, y_rot):
     w = synth.WORKLOADS["r4"]
     x = synth.make_inputs(w, tokens=37)
-    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
 
 
 def test_r4_kronecker_reduced_rows():
@@ -80,7 +93,8 @@ def test_r4_kronecker_reduced_rows():
     run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
 
 
-def test_r3_reduced_query_key():
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_r3_reduced_query_key(kernel_path, y_rot):
     w = synth.WORKLOADS["r3"]
     q, k = synth.make_inputs(w, batch=1, seq=75)
     say("hadamard_rotate Q", tuple(q.shape))
@@ -88,10 +102,10 @@ def test_r3_reduced_query_key():
     yq = hr.rotate(qg, 0)
     torch.cuda.synchronize()
     check_rotated(to_np64(yq).reshape(-1, 128), oracle.rotate(q, 128).reshape(-1, 128), "bf16")
-    run_act(k, 128, 0, hr.QSpec.from_dict(w.qspecs[0]))
+    run_act(k, 128, 0, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
 
 
-def test_weight_reduced_rows():
+def test_weight_reduced_rows(kernel_path):
     w = synth.WORKLOADS["weight"]
     W = synth.make_inputs(w, out_features=300)
     specs = [hr.QSpec.from_dict(d) for d in w.qspecs]
@@ -127,6 +141,38 @@ def test_block_diagonal_rotate_quant(block):
     run_act(x, n, block, hr.QSpec("int", 4, 128, False, "bf16"), y_rot=True)
 
 
+@pytest.mark.parametrize("block", [128, 2048, 4096])
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_specialised_shapes(kernel_path, block, sym, y_rot):
+    """Every compiled shape of the specialised kernels (INT g128 bf16 scales),
+    on a row count that leaves the last wave partly empty."""
+    n = 8192
+    x = synth.gaussian((13, n), seed=2500 + block + sym, dtype=torch.bfloat16)
+    x[3, :] *= 1e3
+    x[4, 100:300] = 0.0
+    run_act(x, n, block, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=y_rot)
+
+
+@pytest.mark.parametrize("w_rot", [False, True])
+@pytest.mark.parametrize("nq", [1, 2])
+def test_weight_variants(kernel_path, w_rot, nq):
+    w = synth.WORKLOADS["weight"]
+    W = synth.make_inputs(w, out_features=77)
+    specs = [hr.QSpec.from_dict(d) for d in w.qspecs][:nq]
+    say("rotate_fuse_weight", tuple(W.shape), specs, "w_rot", w_rot)
+    out = hr.rotate_fuse_weight(W.to(DEV), 0, specs, w_rot=w_rot)
+    torch.cuda.synchronize()
+    y = oracle.rotate(W, 4096)
+    rep = Report()
+    if w_rot:
+        check_rotated(to_np64(out["w_rot"]), y, "bf16", rep)
+    check_mxfp4(out["quant"][0], y, rep)
+    if nq == 2:
+        check_int(out["quant"][1], y, 128, True, "bf16", rep)
+    say("  ", rep)
+
+
 @pytest.mark.parametrize("g", [2, 4, 8, 16, 32, 64, 128, 256, 512, 2048, 8192])
 @pytest.mark.parametrize("sym", [True, False])
 def test_group_sizes(g, sym):
@@ -149,8 +195,8 @@ def test_kronecker_widths(n, dtype):
     run_act(x, n, 0, hr.QSpec("int", 4, 32, True, "bf16"), y_rot=True)
 
 
-@pytest.mark.parametrize("rows", [1, 31, 32, 33, 1001])
-def test_head_dim_rows_ragged_asym(rows):
+@pytest.mark.parametrize("rows", [1, 7, 31, 32, 33, 1001])
+def test_head_dim_rows_ragged_asym(kernel_path, rows):
     # n = 128 with one group per row: zero points pack two rows per byte and an
     # odd total leaves a padded high nibble
     x = synth.gaussian((rows, 128), seed=5000 + rows, dtype=torch.bfloat16)
@@ -160,7 +206,7 @@ def test_head_dim_rows_ragged_asym(rows):
 
 
 @pytest.mark.parametrize("block", [32, 0])
-def test_mxfp4_activations(block):
+def test_mxfp4_activations(kernel_path, block):
     # block-32 rotation with MXFP4 activations (the pages' accuracy setting)
     w = synth.WORKLOADS["r1"]
     x = synth.make_inputs(w, tokens=45)
