@@ -19,8 +19,10 @@ LIB = os.path.join(LIBDIR, "libhadarot.so")
 ARCH = os.environ.get("HADAROT_ARCH", "gfx950")
 
 # Device code: no packed-fp32 instructions (the compiler would otherwise form
-# v_pk_* from ordinary float code); host pass ignores the feature.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# v_pk_* from ordinary float code; the host pass ignores the feature), and MFMA
+# results in ordinary VGPRs (no accumulation-register copies).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
 

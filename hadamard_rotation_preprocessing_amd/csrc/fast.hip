@@ -15,7 +15,7 @@
 //   * lane bits: DPP quad permutations (partner + sign * own);
 //   * otherwise an in-wave transpose through a small padded LDS buffer.
 //
-// kwave<LOGB>: one wave per block of 2^LOGB (2048 or 4096) elements.
+// kwave<LOGB>: one wave per 4096 elements (one 4096 block or two 2048 blocks).
 // k128: eight rows of 128 elements per wave; no LDS at all.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,20 +55,33 @@ __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 
 __device__ __forceinline__ u32x4_t ldg16(const void* p) {
     return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
 }
-__device__ __forceinline__ void stg16(void* p, u32x4_t v) {
-    __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
-}
+// Ordinary stores: a lane's consecutive 16-byte pieces of one cache line are
+// merged in L2 (streaming stores of such partial lines are far slower).
+__device__ __forceinline__ void stg16(void* p, u32x4_t v) { *static_cast<u32x4_t*>(p) = v; }
 
-// A operand H_16: lane l holds H_16[l % 16][4 (l / 16) + t], t = 0..3.
-__device__ __forceinline__ bf16x4_t h16_operand(int lane) {
-    const int i = lane & 15;
-    bf16x4_t h;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int k = 4 * (lane >> 4) + t;
-        h[t] = (__popc(i & k) & 1) ? static_cast<short>(0xBF80) : static_cast<short>(0x3F80);
+// A operand H_16: lane l holds H_16[l % 16][4 (l / 16) + t], t = 0..3, as
+// two dwords of packed bf16 (+1 = 0x3F80, -1 = 0xBF80), element t = 0 lowest.
+struct H16Table {
+    uint32_t w[128];
+    constexpr H16Table() : w() {
+        for (int l = 0; l < 64; ++l)
+            for (int t = 0; t < 4; ++t) {
+                const int i = l & 15, k = 4 * (l >> 4) + t;
+                int p = i & k, par = 0;
+                while (p) {
+                    par ^= p & 1;
+                    p >>= 1;
+                }
+                const uint32_t h = par ? 0xBF80u : 0x3F80u;
+                w[2 * l + (t >> 1)] |= h << (16 * (t & 1));
+            }
     }
-    return h;
+};
+__constant__ constexpr H16Table kH16 = H16Table();
+
+__device__ __forceinline__ bf16x4_t h16_operand(int lane) {
+    const u32x2_t u = {kH16.w[2 * lane], kH16.w[2 * lane + 1]};
+    return __builtin_bit_cast(bf16x4_t, u);
 }
 
 // Transform of the four index bits (k & 3 within the lane, k >> 2 across
@@ -137,15 +150,12 @@ __device__ __forceinline__ uint32_t pack8(const float* t) {
     return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
 }
 
-__device__ __forceinline__ uint32_t bf16x2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
-
-// E2M1 code of v (already divided by the shared scale): nearest of
-// {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even index, saturating; sign
-// set iff v < 0.  Used only for groups whose scale is 2^-127.
-__device__ __forceinline__ uint32_t e2m1_soft(float v) {
-    const float a = fabsf(v);
-    uint32_t i = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-    return i | ((v < 0.0f) ? 8u : 0u);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bfloat16 (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // ------------------------------------------------------------ INT epilogue
@@ -163,7 +173,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
 #pragma unroll
         for (int j = 1; j < E; ++j) am = fmaxf(am, fabsf(u[j]));
         am = lanes_max<GL>(am);
-        s = (am * f) / 7.0f;
+        s = (am * f) * (1.0f / 7.0f);
     } else {
         float hi = u[0], nl = -u[0];
 #pragma unroll
@@ -173,7 +183,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
         }
         hi = fmaxf(lanes_max<GL>(hi), 0.0f) * f;
         nl = fmaxf(lanes_max<GL>(nl), 0.0f) * f;  // -min(min y, 0)
-        s = (hi + nl) / 15.0f;
+        s = (hi + nl) * (1.0f / 15.0f);
         zf = nl;
     }
     uint32_t sbits = 0;
@@ -187,7 +197,9 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
     } else if (s == 0.0f) {
         s = 1.0f;
     }
-    const float inv = f / s;
+    // reciprocal within 1 ulp: moves y / s by about 1e-7 of a step
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float inv = f * rs;
     uint32_t w[E / 8];
     if constexpr (Q::sym) {
         // |y| <= amax and s >= amax / 7 (1 - 2^-8): rne(y / s) stays in [-7, 7],
@@ -202,7 +214,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
             w[b] = pack8(t) ^ 0x88888888u;
         }
     } else {
-        const float z = fminf(fmaxf(rintf(zf / s), 0.0f), 15.0f);
+        const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
         // clamp(rne(y / s) + z, 0, 15): round on y / s alone (ties to even
         // there), clamp to [-z, 15 - z], then add z as an integer.
         const uint32_t zi = static_cast<uint32_t>(z);
@@ -255,6 +267,24 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
 }
 
 // ----------------------------------------------------------- MXFP4 epilogue
+// Eight values -> eight E2M1 nibbles (element 0 lowest) with the hardware
+// converter, which divides by `sc`, rounds to nearest even and saturates.
+__device__ __forceinline__ uint32_t cvt8_fp4(const float* v, float sc, float pre, bool scaled) {
+    uint32_t r = 0;
+    if (scaled) {
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0] * pre, v[1] * pre, sc, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2] * pre, v[3] * pre, sc, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4] * pre, v[5] * pre, sc, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6] * pre, v[7] * pre, sc, 3);
+    } else {
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], sc, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], sc, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], sc, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], sc, 3);
+    }
+    return r;
+}
+
 // y[0..E) contiguous normalised values, E a multiple of 32.
 template <int E>
 __device__ __forceinline__ void epi_mxfp4(const float (&y)[E], const QuantDev& q, int64_t e0, bool valid) {
@@ -270,29 +300,19 @@ __device__ __forceinline__ void epi_mxfp4(const float (&y)[E], const QuantDev& q
         const int ex = static_cast<int>((__float_as_uint(am) >> 23) & 0xFFu);
         const int e = (ex == 0) ? -127 : ex - 129;  // floor(log2 amax) - 2, >= -127
         ebytes |= static_cast<uint32_t>(e + 127) << (8 * g);
-        if (e > -127) {
-            // the converter divides by the scale, rounds to nearest even
-            // and saturates at +-6
-            const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+        // 2^-127 is not a normal float: a group with that scale (amax below
+        // 2^-124) is multiplied by 2^64 and divided by 2^-63 instead, both
+        // exact; the branch is uniform over the wave.
+        if (__builtin_amdgcn_ballot_w64(e == -127) == 0) {
+            const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);  // 2^e
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t r = 0;
-                r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[32 * g + 8 * d + 0], y[32 * g + 8 * d + 1], sc, 0);
-                r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[32 * g + 8 * d + 2], y[32 * g + 8 * d + 3], sc, 1);
-                r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[32 * g + 8 * d + 4], y[32 * g + 8 * d + 5], sc, 2);
-                r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[32 * g + 8 * d + 6], y[32 * g + 8 * d + 7], sc, 3);
-                w[4 * g + d] = r;
-            }
+            for (int d = 0; d < 4; ++d) w[4 * g + d] = cvt8_fp4(y + 32 * g + 8 * d, sc, 1.0f, false);
         } else {
-            // scale 2^-127 (amax below 2^-124): scale by 2^127 in software
-            const float up = __uint_as_float(254u << 23);
+            const bool tiny = e == -127;
+            const float sc = tiny ? __uint_as_float(64u << 23) : __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+            const float pre = tiny ? __uint_as_float(191u << 23) : 1.0f;  // 2^-63 and 2^64
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t r = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) r |= e2m1_soft(y[32 * g + 8 * d + j] * up) << (4 * j);
-                w[4 * g + d] = r;
-            }
+            for (int d = 0; d < 4; ++d) w[4 * g + d] = cvt8_fp4(y + 32 * g + 8 * d, sc, pre, true);
         }
     }
     if (valid) {
@@ -325,39 +345,47 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int LOGB>
+// A wave owns 4096 contiguous elements: one block of 4096 or two of 2048.
 struct KW {
-    static constexpr int B = 1 << LOGB;
-    static constexpr int E = B / 64;          // elements per lane: 32 or 64
+    static constexpr int E = 64;              // elements per lane
     static constexpr int NC = E / 8;          // 16-byte chunks per lane
-    static constexpr int NS = E / 16;         // transpose passes
+    static constexpr int NS = 4;              // transpose passes
     static constexpr int R = 8 / NS;          // chunk elements per pass
-    static constexpr int LW = B / NS;         // elements per pass
-    static constexpr int LDS = LW + (LW >> 5) + 1;
+    static constexpr int LW = 4096 / NS;      // elements per pass
+    static constexpr int LDS_T = LW + (LW >> 5) + 1;     // transpose pass buffer
+    static constexpr int LDS_W = 2048 + (2048 >> 5);      // bf16 words of 4096 outputs
+    static constexpr int LDS = LDS_T > LDS_W ? LDS_T : LDS_W;
     static_assert(LW <= 1024, "padding formula assumes passes of at most 1024 elements");
 };
 
-// One wave per block of B = 2^LOGB elements (bf16 in).  Load layout L0:
-// element e = 512 c + 8 lane + r (chunk c, r = 0..7).  The MFMA transforms
-// bits {0, 1, 7, 8}; register butterflies bits 2 and 9.. ; an LDS transpose
-// (in NS passes over r) gives each lane E contiguous elements; bits 3..6 are
-// then register bits (below log2 E) or lane bits (DPP).
+// Load layout L0: element e = 512 c + 8 lane + r of the wave's 4096 (chunk c,
+// r = 0..7).  The MFMA transforms index bits {0, 1, 7, 8}; register
+// butterflies bits 2, 9, 10 and (4096-blocks) 11; an LDS transpose in NS
+// passes over r gives each lane 64 contiguous elements (L2); bits 3..5 are
+// then register bits and bit 6 is lane bit 0 (DPP).  For 2048-blocks bit 11
+// selects the block and is never mixed.
 template <int LOGB, bool WROT, class Q0, class Q1>
 __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
-    using K = KW<LOGB>;
-    constexpr int B = K::B, E = K::E, NC = K::NC, NS = K::NS, R = K::R;
-    constexpr int LOGE = (E == 64) ? 6 : 5;
-    __shared__ float lds_all[4][K::LDS];
+    static_assert(LOGB == 11 || LOGB == 12, "4096 or 2048 blocks");
+    constexpr int E = KW::E, NC = KW::NC, NS = KW::NS, R = KW::R;
+    constexpr int B = 1 << LOGB;
+    constexpr int BPW = 4096 / B;             // blocks per wave
+    __shared__ float lds_all[4][KW::LDS];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + wv;
-    if (blk >= a.units) return;  // whole wave idle; no barrier follows
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+    const int64_t blk0 = wave * BPW;
+    if (blk0 >= a.units) return;  // whole wave idle; no barrier follows
+    // with two blocks per wave the second may lie past the end
+    const bool hi_ok = BPW == 1 || blk0 + 1 < a.units;
     float* lds = lds_all[wv];
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk * B;
+    const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk0 * B;
 
+    // an absent second block re-reads the first (finite data, never stored)
+    const int hi_off = hi_ok ? 0 : 512 * (NC / 2);
     u32x4_t raw[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane);
+    for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane - (c < NC / 2 ? 0 : hi_off));
 
     const bf16x4_t hop = h16_operand(lane);
     float v[E];
@@ -371,8 +399,9 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
             v[8 * c + 4 + j] = d1[j];
         }
     }
-    // register bits of L0: v-index bit 2 (e bit 2) and bits 3.. (e bits 9..)
-    bfly<E, ~3u & (E - 1)>(v);
+    // register bits of L0: v-index bit 2 (e bit 2), bits 3..5 (e bits 9..11);
+    // e bit 11 only inside a 4096 block
+    bfly<E, (LOGB == 12) ? 0x3Cu : 0x1Cu>(v);
 
     // transpose L0 -> lane-contiguous, in NS passes over r
     float y[E];
@@ -391,16 +420,11 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
             for (int rr = 0; rr < R; ++rr) y[8 * jj + p * R + rr] = lds[rbase + jj * R + rr];
         wave_sync();
     }
-    // bits 3..6: registers below LOGE, lane bits from LOGE on
-    constexpr unsigned regmask = (0x78u) & ((1u << LOGE) - 1u);
-    bfly<E, regmask>(y);
-    if constexpr (LOGE <= 5) dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);      // bit 5
-    if constexpr (LOGE <= 6) {
-        if constexpr (LOGE == 5) dpp_bfly<kXor2>(y, (lane & 2) ? -1.0f : 1.0f);  // bit 6
-        else dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);                      // bit 6
-    }
+    bfly<E, 0x38u>(y);                                   // bits 3, 4, 5
+    dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);       // bit 6
 
-    const int64_t e0 = blk * B + static_cast<int64_t>(E) * lane;
+    const bool valid = hi_ok || lane < 32;
+    const int64_t e0 = blk0 * B + static_cast<int64_t>(E) * lane;
     constexpr bool need_y = WROT || Q0::fmt == 1 || Q1::fmt == 1;
     float f = a.norm;
     if constexpr (need_y) {
@@ -409,14 +433,25 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         f = 1.0f;
     }
     if constexpr (WROT) {
-        uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
+        // bf16 words go back through LDS to the load layout so that each
+        // store instruction writes 1 KiB of consecutive bytes: word
+        // w = 32 lane + m (padded by one per 32) is read back as chunk c,
+        // word k of lane l: w = 256 c + 4 l + k.
+        uint32_t* lw = reinterpret_cast<uint32_t*>(lds);
 #pragma unroll
-        for (int b = 0; b < E / 8; ++b)
-            stg16(dst + 8 * b, u32x4_t{bf16x2(y[8 * b], y[8 * b + 1]), bf16x2(y[8 * b + 2], y[8 * b + 3]),
-                                       bf16x2(y[8 * b + 4], y[8 * b + 5]), bf16x2(y[8 * b + 6], y[8 * b + 7])});
+        for (int m = 0; m < 32; ++m) lw[33 * lane + m] = bf16x2(y[2 * m], y[2 * m + 1]);
+        wave_sync();
+        uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + blk0 * B;
+        const int rb = 4 * lane + (lane >> 3);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4_t wv4 = {lw[rb + 264 * c], lw[rb + 264 * c + 1], lw[rb + 264 * c + 2], lw[rb + 264 * c + 3]};
+            if (c < NC / 2 || hi_ok) stg16(dst + 512 * c + 8 * lane, wv4);
+        }
+        wave_sync();
     }
-    if constexpr (Q0::fmt >= 0) epilogue<E, Q0>(y, f, a.q[0], e0, true, lane, a.total_groups[0]);
-    if constexpr (Q1::fmt >= 0) epilogue<E, Q1>(y, f, a.q[1], e0, true, lane, a.total_groups[1]);
+    if constexpr (Q0::fmt >= 0) epilogue<E, Q0>(y, f, a.q[0], e0, valid, lane, a.total_groups[0]);
+    if constexpr (Q1::fmt >= 0) epilogue<E, Q1>(y, f, a.q[1], e0, valid, lane, a.total_groups[1]);
 }
 
 // ----------------------------------------------------------------- k128
@@ -434,13 +469,12 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
     const int64_t row = (static_cast<int64_t>(blockIdx.x) * 4 + wv) * 8 + (n >> 1);
     const bool valid = row < a.units;
     const int col0 = 32 * h + 8 * qq;  // element of chunk 0 within the row
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + row * 128 + col0;
+    // rows past the end re-read the last row (finite data, never stored)
+    const int64_t lrow = valid ? row : a.units - 1;
+    const uint16_t* src = static_cast<const uint16_t*>(a.x) + lrow * 128 + col0;
     u32x4_t raw[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        if (valid) raw[c] = ldg16(src + 64 * c);
-        else raw[c] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < 2; ++c) raw[c] = ldg16(src + 64 * c);
     const bf16x4_t hop = h16_operand(lane);
     float v[16];
 #pragma unroll
@@ -480,7 +514,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
             am = fmaxf(am, dpp<kXor1>(am));
             am = fmaxf(am, __shfl_xor(am, 16));
             am = fmaxf(am, __shfl_xor(am, 32));
-            s = (am * f) / 7.0f;
+            s = (am * f) * (1.0f / 7.0f);
         } else {
             float hi = v[0], nl = -v[0];
 #pragma unroll
@@ -496,7 +530,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
             nl = fmaxf(nl, __shfl_xor(nl, 32));
             hi = fmaxf(hi, 0.0f) * f;
             nl = fmaxf(nl, 0.0f) * f;
-            s = (hi + nl) / 15.0f;
+            s = (hi + nl) * (1.0f / 15.0f);
             zf = nl;
         }
         uint32_t sbits = 0;
@@ -510,7 +544,8 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
         } else if (s == 0.0f) {
             s = 1.0f;
         }
-        const float inv = f / s;
+        const float rs = __builtin_amdgcn_rcpf(s);
+        const float inv = f * rs;
         uint32_t w[2];
         uint32_t zi = 0;
         if constexpr (Q0::sym) {
@@ -523,7 +558,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
                 w[c] = pack8(t) ^ 0x88888888u;
             }
         } else {
-            const float z = fminf(fmaxf(rintf(zf / s), 0.0f), 15.0f);
+            const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
             zi = static_cast<uint32_t>(z);
             const float lo = kMagic - z, hi = kMagic + 15.0f - z;
 #pragma unroll
@@ -570,7 +605,9 @@ bool qmatch(const FastKey& k, int i) {
 template <int LOGB, bool WROT, class Q0, class Q1>
 int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
     if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || !qmatch<Q1>(k, 1)) return 0;
-    const int64_t grid = (a.units + 3) / 4;
+    constexpr int64_t bpw = 4096 >> LOGB;
+    const int64_t waves = (a.units + bpw - 1) / bpw;
+    const int64_t grid = (waves + 3) / 4;
     hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);

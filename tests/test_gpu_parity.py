@@ -335,3 +335,20 @@ def test_dequant_check(spec):
         # to the bf16 rounding of the reference (2^-8 relative on values of
         # at most 16 steps)
         assert st["max_err_steps"] < 0.5 + 16 * 2.0 ** -8
+
+
+@pytest.mark.parametrize("n,block", [(128, 0), (4096, 0), (8192, 2048), (4096, 512)])
+def test_bf16_outputs_round_to_nearest_even(kernel_path, n, block):
+    """bfloat16 outputs are the round-to-nearest-even of the float32 result:
+    nearly all of them equal the oracle's exact value rounded to bfloat16
+    (differences only where the float32 result and the exact value straddle
+    a rounding midpoint), which truncation or round-half-up would miss on
+    about half or a quarter of the elements."""
+    x = synth.gaussian((64, n), seed=7000 + n + block, dtype=torch.bfloat16)
+    y = hr.rotate(x.to(DEV), block)
+    torch.cuda.synchronize()
+    ref = oracle.bf16_round(oracle.rotate(x, n, block))
+    got = to_np64(y)
+    frac = float(np.mean(got == ref))
+    say("bf16 outputs equal to RNE(exact):", frac)
+    assert frac > 0.999
