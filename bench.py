@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
 METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
+COPY_BYTES = 256 * 1024 * 1024
 
 
 def sources_digest() -> str:
@@ -171,11 +172,14 @@ def traffic_for(kernel: str, digest: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling)" % ",".join(PARTS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 64)
+    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 8)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 256 MiB device copy three times "
+                         "(reference for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path shards rows across GPUs with no communication, "
@@ -217,6 +221,13 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_per_step = total_ms / args.steps
 
     step_bytes = sum(parts[nm]["bytes"] for nm in names)

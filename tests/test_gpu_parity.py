@@ -87,10 +87,29 @@ def test_r4_reduced_rows(kernel_path, y_rot):
     run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
 
 
-def test_r4_kronecker_reduced_rows():
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_r4_kronecker_reduced_rows(kernel_path, y_rot):
     w = synth.WORKLOADS["r4_kron"]
     x = synth.make_inputs(w, tokens=13)
-    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=True)
+    run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
+
+
+@pytest.mark.parametrize("k", [12, 20, 28])
+@pytest.mark.parametrize("mode", ["rotate", "sym", "asym", "asym+rot", "sym+rot"])
+def test_kronecker_512_pieces(kernel_path, k, mode):
+    """Widths K x 512 (the compiled Kronecker shapes) in every mode."""
+    n = k * 512
+    x = synth.gaussian((9, n), seed=8000 + k, dtype=torch.bfloat16)
+    x[2] *= 1e-3
+    x[5, :700] = 0.0
+    if mode == "rotate":
+        say("hadamard_rotate (Kronecker)", 9, n)
+        y = hr.rotate(x.to(DEV), 0)
+        torch.cuda.synchronize()
+        check_rotated(to_np64(y), oracle.rotate(x, n), "bf16")
+        return
+    sym = mode.startswith("sym")
+    run_act(x, n, 0, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=mode.endswith("+rot"))
 
 
 @pytest.mark.parametrize("y_rot", [False, True])
@@ -352,3 +371,64 @@ def test_bf16_outputs_round_to_nearest_even(kernel_path, n, block):
     frac = float(np.mean(got == ref))
     say("bf16 outputs equal to RNE(exact):", frac)
     assert frac > 0.999
+
+
+E2M1_TIES = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, 0.125, 3.0, 7.0]
+
+
+@pytest.mark.parametrize("path", ["act", "weight"])
+def test_mxfp4_exact_ties(kernel_path, path):
+    """Rows with two nonzero inputs x[0] = a, x[1] = b rotate (n = 4096,
+    1/sqrt(n) = 2^-6) to the exact values (a + b)/64 at even and (a - b)/64 at
+    odd positions, so the quantizer input is known exactly and the codes must
+    equal the oracle's bit for bit: every E2M1 rounding tie (ties to the even
+    mantissa), saturation above 6 and negative values (sign kept)."""
+    n = 4096
+    rows = []
+    for e in (-3, 0, 4):
+        for t in E2M1_TIES:
+            for sgn in (1.0, -1.0):
+                hi, lo = 6.0 * 2.0 ** e, sgn * t * 2.0 ** e   # amax = 6 2^e -> shared exponent e
+                a, b = 32.0 * (hi + lo), 32.0 * (hi - lo)
+                r = np.zeros(n)
+                r[0], r[1] = a, b
+                rows.append(r)
+    x64 = np.array(rows)
+    x = torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(x.to(torch.float64).numpy(), x64), "inputs must be exact in bf16"
+    y = oracle.rotate(x, n)
+    assert np.array_equal(y[:, 0], (x64[:, 0] + x64[:, 1]) / 64)
+    spec = hr.QSpec.mxfp4()
+    if path == "act":
+        out = hr.rotate_quantize_act(x.to(DEV), 0, spec)
+    else:
+        out = hr.rotate_fuse_weight(x.to(DEV), 0, [spec], w_rot=False)["quant"][0]
+    torch.cuda.synchronize()
+    ref = oracle.mxfp4_quant(y, 32)
+    codes = oracle.unpack_nibbles(out["codes"].cpu().numpy().reshape(-1), y.size).reshape(y.shape)
+    assert np.array_equal(out["scales"].cpu().numpy().astype(np.int64).reshape(ref.scales.shape), ref.scales)
+    assert np.array_equal(codes, ref.codes)
+
+
+def test_int4_exact_ties(kernel_path):
+    """Two-nonzero rows as above with amax = 7 2^m (so s = 2^m exactly) and the
+    other value at (k + 1/2) 2^m: every symmetric rounding tie, both signs."""
+    n = 4096
+    rows = []
+    for m in (-5, 0, 3):
+        for k in range(-7, 7):
+            hi, lo = 7.0 * 2.0 ** m, (k + 0.5) * 2.0 ** m
+            r = np.zeros(n)
+            r[0], r[1] = 32.0 * (hi + lo), 32.0 * (hi - lo)
+            rows.append(r)
+    x64 = np.array(rows)
+    x = torch.from_numpy(x64.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(x.to(torch.float64).numpy(), x64)
+    y = oracle.rotate(x, n)
+    spec = hr.QSpec("int", 4, 128, True, "bf16")
+    out = hr.rotate_quantize_act(x.to(DEV), 0, spec)
+    torch.cuda.synchronize()
+    ref = oracle.rtn_quant(y, 128, 4, True, "bf16")
+    codes = oracle.unpack_nibbles(out["codes"].cpu().numpy().reshape(-1), y.size, signed=True).reshape(y.shape)
+    assert np.array_equal(to_np64(out["scales"]).reshape(ref.scales.shape), ref.scales)
+    assert np.array_equal(codes, ref.codes)
