@@ -231,9 +231,10 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     return HR_OK;
 }
 
-// Specialised bf16 kernels (one wave per 128-, 2048- or 4096-element block)
-// take the call when one is compiled for its exact shape; the generic kernel
-// runs otherwise, or always when HADAROT_FORCE_GENERIC=1.
+// Specialised bf16 kernels (one wave per 128-, 2048- or 4096-element block;
+// one workgroup per Kronecker row of K x 512) take the call when one is
+// compiled for its exact shape; the generic kernel runs otherwise, or always
+// when HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
     const hr::RotArgs& a = p.a;
@@ -259,6 +260,31 @@ int run(const hr::RotPlan& p, void* stream) {
         f.units = a.total_chunks;
         f.norm = a.norm;
         const int r = hr::launch_fast(k, f, stream);
+        if (r == 1) return ok();
+        if (r < 0)
+            return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));
+    }
+    if (!generic_only && p.bf16 && a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9 && a.nq <= 1) {
+        hr::FastKey k{};
+        hr::KronArgs ka{};
+        k.logb = a.logb;
+        k.wrot = a.y_rot != nullptr;
+        k.nq = a.nq;
+        if (a.nq == 1) {
+            k.fmt[0] = a.q[0].format;
+            k.sym[0] = a.q[0].sym;
+            k.logg[0] = a.q[0].logg;
+            k.sdt[0] = a.q[0].scale_dtype;
+            ka.q = a.q[0];
+            ka.total_groups = a.total_groups[0];
+        }
+        ka.x = a.x;
+        ka.y_rot = a.y_rot;
+        ka.rows = a.total_chunks;
+        ka.norm = a.norm;
+        ka.k = a.kron_k;
+        for (int c = 0; c < a.kron_k; ++c) ka.hk_neg[c] = static_cast<uint32_t>(a.hk_neg[c]);
+        const int r = hr::launch_kron(k, ka, stream);
         if (r == 1) return ok();
         if (r < 0)
             return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));

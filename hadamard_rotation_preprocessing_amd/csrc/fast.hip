@@ -159,9 +159,10 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
 }
 
 // ------------------------------------------------------------ INT epilogue
-// u[0..E) are the lane's E contiguous elements of one group of G >= E
-// elements spread over GL = G / E lanes; y = u * f.
-template <int E, class Q>
+// u[0..E) are the lane's E elements of one group of G >= E elements spread
+// over GL = G / E lanes, as E / 8 runs of 8 consecutive elements, run b
+// starting at element e0 + b SR (SR = 8: E contiguous elements); y = u * f.
+template <int E, class Q, int SR = 8>
 __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const QuantDev& q, int64_t e0, bool valid,
                                         int lane, int64_t total_groups) {
     constexpr int G = 1 << Q::logg;
@@ -247,7 +248,10 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
     }
     if (valid) {
         uint8_t* cp = q.codes + (e0 >> 1);
-        if constexpr (E / 8 == 8) {
+        if constexpr (SR != 8) {
+#pragma unroll
+            for (int b = 0; b < E / 8; ++b) *reinterpret_cast<uint32_t*>(cp + (b * SR) / 2) = w[b];
+        } else if constexpr (E / 8 == 8) {
             stg16(cp, u32x4_t{w[0], w[1], w[2], w[3]});
             stg16(cp + 16, u32x4_t{w[4], w[5], w[6], w[7]});
         } else if constexpr (E / 8 == 4) {
@@ -593,6 +597,142 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
     }
 }
 
+// ----------------------------------------------------------------- kkron
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// One workgroup (4 waves) per row of n = K * 512 bf16 elements, K <= 32,
+// computing y = x (H_K (x) H_512) / sqrt(n) (AutoRound "Rotation Transform",
+// section 1.5: base matrix of order K combined with a Sylvester block).
+// Phase 1: the row is staged in LDS as bf16 (rows a >= K zero).
+// Phase 2: Y'[c][b] = sum_a H_K[a][c] x[a][b] with v_mfma_f32_32x32x8_bf16:
+//   A is 32 columns b by 8 pieces a of x gathered from LDS, B the +-1 slice
+//   of H_K (zero outside K); bf16 times +-1 is exact, accumulation float32.
+//   Wave w takes column tiles w, w+4, w+8, w+12; lane l then holds 64 values
+//   of piece c = l % 32 whose column bits {0,1,3,4,7,8} are register bits:
+//   six stages of the length-512 transform in registers.
+// Phase 3 (two passes of 16 pieces): an LDS exchange gives 16 lanes per
+//   piece, 32 values per lane, column bits {0,1,2,5,6} in registers: the
+//   stages for bits 2, 5, 6, then the epilogue (groups of 128 over 4 lanes).
+template <int K, bool WROT, class Q0>
+__global__ void __launch_bounds__(256) kkron(const KronArgs a) {
+    static_assert(K <= 32, "one MFMA K-padding of 32");
+    constexpr int M = 512;
+    constexpr int n = K * M;
+    constexpr int XS = 520;   // staging row stride, bf16 units (260 dwords)
+    constexpr int YS = 519;   // exchange row stride, floats; index c YS + b + (b >> 6)
+    constexpr int SM = 16 * YS + 16;
+    static_assert(SM >= 32 * XS / 2, "staging fits in the exchange buffer");
+    __shared__ float smem[SM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int64_t row = blockIdx.x;
+    uint32_t* xs32 = reinterpret_cast<uint32_t*>(smem);
+    const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(smem);
+
+    // ---- phase 1: stage the row (16-byte chunks, row a at dword 260 a)
+    {
+        constexpr int NQ = K * 64;                    // 16-byte chunks per row
+        constexpr int PER = (NQ + 255) / 256;
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + row * n;
+        u32x4_t v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + 256 * k;
+            v[k] = ldg16(src + 8 * (q < NQ ? q : 0));
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + 256 * k;
+            if (q < NQ) *reinterpret_cast<u32x4_t*>(xs32 + 260 * (q >> 6) + 4 * (q & 63)) = v[k];
+        }
+        for (int q = 260 * K + tid; q < 260 * 32; q += 256) xs32[q] = 0u;
+    }
+    __syncthreads();
+
+    // ---- phase 2: base-matrix mix on the MFMA, then six register stages
+    const int bl = lane & 31;
+    const int h = lane >> 5;
+    u32x2_t hb[4];
+    {
+        const uint32_t neg = (bl < K) ? a.hk_neg[bl] : 0u;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            uint32_t d[2] = {0u, 0u};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int ai = 8 * st + 4 * h + t;
+                const uint32_t val = (ai < K && bl < K) ? (((neg >> ai) & 1u) ? 0xBF80u : 0x3F80u) : 0u;
+                d[t >> 1] |= val << (16 * (t & 1));
+            }
+            hb[st] = u32x2_t{d[0], d[1]};
+        }
+    }
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tile = w + 4 * i;
+        f32x16_t d = {};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int base = (8 * st + 4 * h) * XS + 32 * tile + bl;
+            const uint32_t lo = static_cast<uint32_t>(xs16[base]) | (static_cast<uint32_t>(xs16[base + XS]) << 16);
+            const uint32_t hi = static_cast<uint32_t>(xs16[base + 2 * XS]) | (static_cast<uint32_t>(xs16[base + 3 * XS]) << 16);
+            const u32x2_t av = {lo, hi};
+            d = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(bf16x4_t, av),
+                                                          __builtin_bit_cast(bf16x4_t, hb[st]), d, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[16 * i + r] = d[r];
+    }
+    // v[16 i + r] is piece c = bl at column b = 32 (w + 4 i) + 8 (r >> 2) + 4 h + (r & 3)
+    bfly<64, 0x3Fu>(v);
+    __syncthreads();  // all gathers done: the staging buffer is free
+
+    // ---- phase 3: exchange in two passes of 16 pieces
+    const int L = lane & 15;
+    const int g = lane >> 4;
+    const int wb = 4 * h + 32 * w + (w >> 1);
+#pragma unroll
+    for (int pass = 0; pass < (K + 15) / 16; ++pass) {
+        const int cw = bl - 16 * pass;
+        if (cw >= 0 && cw < 16 && bl < K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) smem[cw * YS + wb + 130 * i + 8 * (r >> 2) + (r & 3)] = v[16 * i + r];
+        }
+        __syncthreads();
+        const int cp = 4 * w + g;                 // piece within the pass
+        const int c2 = 16 * pass + cp;            // piece
+        const bool valid = c2 < K;
+        const int rb = (valid ? cp : 0) * YS + 8 * (L & 3) + 130 * (L >> 2);
+        float u[32];
+#pragma unroll
+        for (int jh = 0; jh < 4; ++jh)
+#pragma unroll
+            for (int jl = 0; jl < 8; ++jl) u[8 * jh + jl] = smem[rb + jl + 32 * jh + (jh >> 1)];
+        __syncthreads();  // before the next pass overwrites the buffer
+        bfly<32, 0x1Cu>(u);   // column bits 2, 5, 6
+
+        // u[8 jh + jl] is column b = 8 (L & 3) + 32 jh + 128 (L >> 2) + jl of piece c2
+        const int64_t e0 = row * n + c2 * M + 8 * (L & 3) + 128 * (L >> 2);
+        if constexpr (WROT) {
+            float y[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) y[j] = u[j] * a.norm;
+            if (valid) {
+                uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
+#pragma unroll
+                for (int jh = 0; jh < 4; ++jh)
+                    stg16(dst + 32 * jh, u32x4_t{bf16x2(y[8 * jh], y[8 * jh + 1]), bf16x2(y[8 * jh + 2], y[8 * jh + 3]),
+                                                 bf16x2(y[8 * jh + 4], y[8 * jh + 5]), bf16x2(y[8 * jh + 6], y[8 * jh + 7])});
+            }
+        }
+        if constexpr (Q0::fmt == 0) epi_int<32, Q0, 32>(u, a.norm, a.q, e0, valid, lane, a.total_groups);
+    }
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <class Q>
@@ -622,6 +762,14 @@ int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
 
+template <int K, bool WROT, class Q0>
+int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
+    if (a.k != K || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
+    hipLaunchKernelGGL((kkron<K, WROT, Q0>), dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 1 : -static_cast<int>(e);
+}
+
 using IS128B = QD<0, 1, 7, 1>;   // INT sym g128 bf16 scales
 using IA128B = QD<0, 0, 7, 1>;   // INT asym g128 bf16 scales
 using IS128F = QD<0, 1, 7, 0>;
@@ -629,6 +777,27 @@ using IA128F = QD<0, 0, 7, 0>;
 using MX = QD<1, 1, 5, 2>;       // MXFP4
 
 }  // namespace
+int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k.logb != 9) return 0;
+    int r = 0;
+#define HR_TRY(expr) \
+    if ((r = (expr)) != 0) return r
+    HR_TRY((try_kkron<28, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, true, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, true, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<12, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<12, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<12, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<20, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<20, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<20, true, QNone>(k, a, s)));
+#undef HR_TRY
+    return 0;
+}
+
 
 int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -82,6 +82,18 @@ struct FastArgs {
     QuantDev q[kMaxQuant];
 };
 
+// Arguments of the specialised Kronecker kernel (rows of K * 512 bf16).
+struct KronArgs {
+    const void* x;
+    void* y_rot;              // nullable
+    int64_t rows;
+    int64_t total_groups;
+    float norm;               // 1/sqrt(K * 512)
+    int32_t k;                // base order, <= 32
+    QuantDev q;
+    uint32_t hk_neg[32];      // bit a of hk_neg[c] set iff H_K[a][c] == -1
+};
+
 // Compile-time shape of a specialised kernel, matched at dispatch.
 struct FastKey {
     int logb;                 // 7, 11 or 12
@@ -94,6 +106,10 @@ int launch_rotate(const RotPlan& p, void* stream);        // returns hipError_t
 // Launches a specialised kernel if one matches `k`: returns 1 if launched,
 // 0 if none matches, or a negative hipError_t on a launch error.
 int launch_fast(const FastKey& k, const FastArgs& a, void* stream);
+// Launches the specialised Kronecker kernel if one matches (K <= 32,
+// M = 512, bf16, no quantizer or INT g128 with bf16 scales): 1 launched,
+// 0 no match, negative hipError_t on a launch error.
+int launch_kron(const FastKey& k, const KronArgs& a, void* stream);
 int launch_dequant(const DqArgs& a, void* stream);        // returns hipError_t
 
 }  // namespace hr
