@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "plan.h"
 
 namespace hr {
@@ -38,6 +40,8 @@ constexpr int kXor1 = 0xB1;        // DPP quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;        // DPP quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141; // lane i <-> 7 - i within 8
 constexpr int kMirror = 0x140;     // lane i <-> 15 - i within 16
+
+constexpr int kMaxDevices = 64;
 
 template <int FMT, int SYM, int LOGG, int SDT>
 struct QD {
@@ -599,137 +603,289 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
 
 // ----------------------------------------------------------------- kkron
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Hides a value from the optimiser, so that per-lane LDS bases stay whole
+// and the constant parts of addresses stay in the instruction offsets.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// (lanes 0-31 of x, lanes 0-31 of y), (lanes 32-63 of x, lanes 32-63 of y)
+__device__ __forceinline__ void swap_halves(float& x, float& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+// maximum of v over lanes l and l ^ 32
+__device__ __forceinline__ float max_halves(float v) {
+    float a = v, b = v;
+    swap_halves(a, b);
+    return fmaxf(a, b);
+}
 
 // One workgroup (4 waves) per row of n = K * 512 bf16 elements, K <= 32,
 // computing y = x (H_K (x) H_512) / sqrt(n) (AutoRound "Rotation Transform",
-// section 1.5: base matrix of order K combined with a Sylvester block).
-// Phase 1: the row is staged in LDS as bf16 (rows a >= K zero).
-// Phase 2: Y'[c][b] = sum_a H_K[a][c] x[a][b] with v_mfma_f32_32x32x8_bf16:
-//   A is 32 columns b by 8 pieces a of x gathered from LDS, B the +-1 slice
-//   of H_K (zero outside K); bf16 times +-1 is exact, accumulation float32.
-//   Wave w takes column tiles w, w+4, w+8, w+12; lane l then holds 64 values
-//   of piece c = l % 32 whose column bits {0,1,3,4,7,8} are register bits:
-//   six stages of the length-512 transform in registers.
-// Phase 3 (two passes of 16 pieces): an LDS exchange gives 16 lanes per
-//   piece, 32 values per lane, column bits {0,1,2,5,6} in registers: the
-//   stages for bits 2, 5, 6, then the epilogue (groups of 128 over 4 lanes).
+// section 1.5: a base matrix of order K combined with a Sylvester block).
+// Write the row as x[a][b] (piece a < K, column b < 512, bits b0..b8).
+// Phase 1: stage the row in LDS, 16 bytes per (piece octet, column): dword j
+//   of octet q at column b holds x[8q + 2j][b] (low half) and x[8q + 2j + 1][b];
+//   pieces >= K are zero. Within each run of 8 columns the 16-byte slots are
+//   XOR-swizzled so that both the staging writes and the operand reads are
+//   free of bank conflicts.
+// Phase 2: v_mfma_f32_32x32x16_bf16 contracts over (u, a) at once, u being
+//   column bits b6..b8: for output bits s and piece c,
+//   Y[c][i + 32 blk + 64 s] = sum_u sum_a H_8[u][s] H_K[a][c] x[a][i + 32 blk + 64 u]
+//   (i = b0..b4, blk = b5). A = 32 columns i by 16 pieces a of x (one u, one
+//   16-byte read per lane), B = +-H_K slice (the sign H_8[u][s] picks the
+//   copy). bf16 times +-1 is exact; the sum is float32. This takes the
+//   base-matrix mix and three of the nine column stages. Wave w owns output
+//   bits (b7, b8) = (w & 1, w >> 1) and all of b0..b6: four tiles (blk, b6).
+//   Lane l then holds piece c = l % 32, b2 = l / 32, and b0, b1, b3, b4, b5
+//   in registers: five butterfly stages, then one across the two half-waves
+//   (v_permlane32_swap) for b2, after which lane l holds the 64 consecutive
+//   columns of piece c with b6 = l / 32.
+// Epilogue: a group of 128 columns (b0..b6) sits in lanes l and l ^ 32.
+template <int W, int HALVES>
+__device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float (&v)[64]) {
+    constexpr int BT = 8192;                 // B table offset, dwords
+    const int il = lane & 31;
+    const int g = lane >> 5;
+    // B operand: lane (c, g) element t = H_K[16 h + 8 g + t][c]
+    u32x4_t bp[HALVES], bn[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t x = smem[BT + lane + 64 * (p + 4 * h)];
+            bp[h][p] = x;
+            bn[h][p] = x ^ 0x80008000u;
+        }
+    }
+    // A operand: lane (i, g) element t = x[16 h + 8 g + t][i + 32 blk + 64 u],
+    // the 16-byte slot of octet 2 h + g at the swizzled column
+    const u32x4_t* ab[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int hs = ((il >> 3) + 4 * blk) & 7;
+        ab[blk] = reinterpret_cast<const u32x4_t*>(smem + opaque(4 * (g * 512 + (il & ~7) + 32 * blk + ((il & 7) ^ hs))));
+    }
+    f32x16_t d[4];   // tile blk + 2 b6
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[blk][2 * h * 512 + 64 * u]);
+#pragma unroll
+                for (int s0 = 0; s0 < 2; ++s0) {
+                    const int s = s0 + 2 * W;
+                    const bool neg = __builtin_popcount(u & s) & 1;
+                    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, neg ? bn[h] : bp[h]);
+                    f32x16_t& acc = d[blk + 2 * s0];
+                    if (u == 0 && h == 0)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16_t{}, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[16 * t + r] = d[t][r];
+}
+
+// Element index of column 8 m + q (m, q < 8) within the lane's 64-column run.
+__host__ __device__ constexpr int kron_elem(int m, int q) {
+    return (q & 3) | ((m & 3) << 2) | ((m >> 2) << 4) | ((q >> 2) << 5);
+}
+
+// INT4 g128 epilogue of the lane's 64 consecutive columns (the other 64 of
+// the group in lane l ^ 32). Arithmetic as in epi_int. cp: the 32 code bytes;
+// gidx: group index; zslot: LDS byte for the zero point (asymmetric).
+template <class Q>
+__device__ __forceinline__ void epi_kron(const float (&u)[64], float f, const QuantDev& q, uint8_t* cp, int64_t gidx,
+                                         bool valid, bool first, uint8_t* zslot) {
+    static_assert(Q::logg == 7, "groups of 128 columns");
+    float s, zf = 0.0f;
+    if constexpr (Q::sym) {
+        float am = fabsf(u[0]);
+#pragma unroll
+        for (int j = 1; j < 64; ++j) am = fmaxf(am, fabsf(u[j]));
+        am = max_halves(am);
+        s = (am * f) * (1.0f / 7.0f);
+    } else {
+        float hi = u[0], nl = -u[0];
+#pragma unroll
+        for (int j = 1; j < 64; ++j) {
+            hi = fmaxf(hi, u[j]);
+            nl = fmaxf(nl, -u[j]);
+        }
+        // after the swap, max(hi, nl) is the group's max y in lanes 0-31 and
+        // its -min y in lanes 32-63; a second swap hands each to every lane
+        swap_halves(hi, nl);
+        float mhi = fmaxf(hi, nl);
+        float mnl = mhi;
+        swap_halves(mhi, mnl);
+        hi = fmaxf(mhi, 0.0f) * f;
+        nl = fmaxf(mnl, 0.0f) * f;  // -min(min y, 0)
+        s = (hi + nl) * (1.0f / 15.0f);
+        zf = nl;
+    }
+    uint32_t sbits = f2bf(s);
+    s = bf2f(sbits);
+    if (s == 0.0f) {
+        s = 1.0f;
+        sbits = 0x3F80u;
+    }
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float inv = f * rs;
+    uint32_t w[8];
+    if constexpr (Q::sym) {
+        const float off = kMagic + 8.0f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            float t[8];
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) t[qq] = fmaf(u[kron_elem(m, qq)], inv, off);
+            w[m] = pack8(t) ^ 0x88888888u;
+        }
+    } else {
+        const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
+        const uint32_t zi = static_cast<uint32_t>(z);
+        const float lo = kMagic - z, hi = kMagic + 15.0f - z;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            float t[8];
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const float r = __builtin_amdgcn_fmed3f(fmaf(u[kron_elem(m, qq)], inv, kMagic), lo, hi);
+                t[qq] = __uint_as_float(__float_as_uint(r) + zi);
+            }
+            w[m] = pack8(t);
+        }
+        if (first) *zslot = static_cast<uint8_t>(zi);
+    }
+    if (valid) {
+        stg16(cp, u32x4_t{w[0], w[1], w[2], w[3]});
+        stg16(cp + 16, u32x4_t{w[4], w[5], w[6], w[7]});
+        if (first) static_cast<uint16_t*>(q.scales)[gidx] = static_cast<uint16_t>(sbits);
+    }
+}
+
 template <int K, bool WROT, class Q0>
-__global__ void __launch_bounds__(256) kkron(const KronArgs a) {
+__global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
     static_assert(K <= 32, "one MFMA K-padding of 32");
     constexpr int M = 512;
     constexpr int n = K * M;
-    constexpr int XS = 520;   // staging row stride, bf16 units (260 dwords)
-    constexpr int YS = 519;   // exchange row stride, floats; index c YS + b + (b >> 6)
-    constexpr int SM = 16 * YS + 16;
-    static_assert(SM >= 32 * XS / 2, "staging fits in the exchange buffer");
-    __shared__ float smem[SM];
+    constexpr int HALVES = K > 16 ? 2 : 1;   // 16-piece halves of the contraction
+    constexpr int BT = 8192;                 // B table offset, dwords (staging below)
+    constexpr int ZB = BT + 512;             // zero-point bytes, 4 per piece
+    __shared__ uint32_t smem[ZB + 32];
+    uint8_t* zbuf = reinterpret_cast<uint8_t*>(smem + ZB);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int64_t row = blockIdx.x;
-    uint32_t* xs32 = reinterpret_cast<uint32_t*>(smem);
-    const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(smem);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const bool stager = w < 2 * HALVES;
 
-    // ---- phase 1: stage the row (16-byte chunks, row a at dword 260 a)
-    {
-        constexpr int NQ = K * 64;                    // 16-byte chunks per row
-        constexpr int PER = (NQ + 255) / 256;
-        const uint16_t* src = static_cast<const uint16_t*>(a.x) + row * n;
-        u32x4_t v[PER];
+    // Wave w < 2 HALVES loads piece octet w of a row: columns 8 lane .. 8 lane + 7.
+    u32x4_t ld[8];
+    auto load = [&](int64_t r) {
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * n + 8 * lane;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int q = tid + 256 * k;
-            v[k] = ldg16(src + 8 * (q < NQ ? q : 0));
+        for (int j = 0; j < 8; ++j) {
+            if (8 * w + j < K) ld[j] = ldg16(src + (8 * w + j) * M);
+            else ld[j] = u32x4_t{0u, 0u, 0u, 0u};
         }
+    };
+
+    // B table entry e = lane' + 64 (p + 4 h): H_K[16 h + 8 g + 2p (+1)][c]
+    // for c = lane' % 32, g = lane' / 32, as packed bf16 +-1. Never overwritten.
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int q = tid + 256 * k;
-            if (q < NQ) *reinterpret_cast<u32x4_t*>(xs32 + 260 * (q >> 6) + 4 * (q & 63)) = v[k];
-        }
-        for (int q = 260 * K + tid; q < 260 * 32; q += 256) xs32[q] = 0u;
+    for (int k = 0; k < 2; ++k) {
+        const int e = tid + 256 * k;
+        const int c = e & 31, g = (e >> 5) & 1, p = (e >> 6) & 3, h = e >> 8;
+        const uint32_t nb = a.hk_neg[c] >> (16 * h + 8 * g + 2 * p);
+        smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
     }
-    __syncthreads();
 
-    // ---- phase 2: base-matrix mix on the MFMA, then six register stages
-    const int bl = lane & 31;
-    const int h = lane >> 5;
-    u32x2_t hb[4];
-    {
-        const uint32_t neg = (bl < K) ? a.hk_neg[bl] : 0u;
+    // Rows blockIdx.x, blockIdx.x + gridDim.x, ...: the next row's loads are
+    // in flight while the current row is transformed.
+    int64_t row = blockIdx.x;
+    const int64_t stride = gridDim.x;
+    const int c = lane & 31;                   // piece
+    const int g = lane >> 5;                   // column bit b6 after the mix
+    const bool valid = c < K;
+    if (stager) load(row);
+    for (;;) {
+        // ---- phase 1: stage the row (16-byte slot of column 8 lane + cc at
+        // 8 lane + (cc ^ (lane & 7)) within octet w), then prefetch the next
+        if (stager) {
+            const int base = 16 * (w * 512 + 8 * lane);     // bytes
+            const int hs16 = 16 * (lane & 7);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            uint32_t d[2] = {0u, 0u};
+            for (int cc = 0; cc < 8; ++cc) {
+                const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                u32x4_t o;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int ai = 8 * st + 4 * h + t;
-                const uint32_t val = (ai < K && bl < K) ? (((neg >> ai) & 1u) ? 0xBF80u : 0x3F80u) : 0u;
-                d[t >> 1] |= val << (16 * (t & 1));
+                for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(ld[2 * j + 1][cc >> 1], ld[2 * j][cc >> 1], sel);
+                *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(smem) + ((base | hs16) ^ (16 * cc))) = o;
             }
-            hb[st] = u32x2_t{d[0], d[1]};
         }
-    }
-    float v[64];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tile = w + 4 * i;
-        f32x16_t d = {};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int base = (8 * st + 4 * h) * XS + 32 * tile + bl;
-            const uint32_t lo = static_cast<uint32_t>(xs16[base]) | (static_cast<uint32_t>(xs16[base + XS]) << 16);
-            const uint32_t hi = static_cast<uint32_t>(xs16[base + 2 * XS]) | (static_cast<uint32_t>(xs16[base + 3 * XS]) << 16);
-            const u32x2_t av = {lo, hi};
-            d = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(bf16x4_t, av),
-                                                          __builtin_bit_cast(bf16x4_t, hb[st]), d, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[16 * i + r] = d[r];
-    }
-    // v[16 i + r] is piece c = bl at column b = 32 (w + 4 i) + 8 (r >> 2) + 4 h + (r & 3)
-    bfly<64, 0x3Fu>(v);
-    __syncthreads();  // all gathers done: the staging buffer is free
-
-    // ---- phase 3: exchange in two passes of 16 pieces
-    const int L = lane & 15;
-    const int g = lane >> 4;
-    const int wb = 4 * h + 32 * w + (w >> 1);
-#pragma unroll
-    for (int pass = 0; pass < (K + 15) / 16; ++pass) {
-        const int cw = bl - 16 * pass;
-        if (cw >= 0 && cw < 16 && bl < K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) smem[cw * YS + wb + 130 * i + 8 * (r >> 2) + (r & 3)] = v[16 * i + r];
-        }
+        const int64_t next = row + stride;
+        if (stager && next < a.rows) load(next);
         __syncthreads();
-        const int cp = 4 * w + g;                 // piece within the pass
-        const int c2 = 16 * pass + cp;            // piece
-        const bool valid = c2 < K;
-        const int rb = (valid ? cp : 0) * YS + 8 * (L & 3) + 130 * (L >> 2);
-        float u[32];
-#pragma unroll
-        for (int jh = 0; jh < 4; ++jh)
-#pragma unroll
-            for (int jl = 0; jl < 8; ++jl) u[8 * jh + jl] = smem[rb + jl + 32 * jh + (jh >> 1)];
-        __syncthreads();  // before the next pass overwrites the buffer
-        bfly<32, 0x1Cu>(u);   // column bits 2, 5, 6
 
-        // u[8 jh + jl] is column b = 8 (L & 3) + 32 jh + 128 (L >> 2) + jl of piece c2
-        const int64_t e0 = row * n + c2 * M + 8 * (L & 3) + 128 * (L >> 2);
-        if constexpr (WROT) {
-            float y[32];
+        // ---- phase 2: mix on the MFMA, five register stages, one across halves
+        float v[64];
+        switch (w) {
+            case 0: kkron_mix<0, HALVES>(smem, lane, v); break;
+            case 1: kkron_mix<1, HALVES>(smem, lane, v); break;
+            case 2: kkron_mix<2, HALVES>(smem, lane, v); break;
+            default: kkron_mix<3, HALVES>(smem, lane, v); break;
+        }
+        // v[16 (blk + 2 b6) + r]: column b0, b1 = r & 3, b3, b4 = r >> 2, b5 = blk; b2 = lane / 32
+        bfly<64, 0x1Fu>(v);
 #pragma unroll
-            for (int j = 0; j < 32; ++j) y[j] = u[j] * a.norm;
+        for (int j = 0; j < 32; ++j) {
+            float x0 = v[j], x1 = v[j + 32];
+            swap_halves(x0, x1);      // (b6 = lane / 32; b2 = 0, 1)
+            v[j] = x0 + x1;
+            v[j + 32] = x0 - x1;
+        }
+        // v[j]: column 8 m + q of the run of 64 starting at 64 (g + 2 w),
+        // with j = kron_elem(m, q)
+        const int64_t e0 = row * n + c * M + 64 * (g + 2 * w);
+        if constexpr (WROT) {
             if (valid) {
                 uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
 #pragma unroll
-                for (int jh = 0; jh < 4; ++jh)
-                    stg16(dst + 32 * jh, u32x4_t{bf16x2(y[8 * jh], y[8 * jh + 1]), bf16x2(y[8 * jh + 2], y[8 * jh + 3]),
-                                                 bf16x2(y[8 * jh + 4], y[8 * jh + 5]), bf16x2(y[8 * jh + 6], y[8 * jh + 7])});
+                for (int m = 0; m < 8; ++m) {
+                    u32x4_t o;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        o[p] = bf16x2(v[kron_elem(m, 2 * p)] * a.norm, v[kron_elem(m, 2 * p + 1)] * a.norm);
+                    stg16(dst + 8 * m, o);
+                }
             }
         }
-        if constexpr (Q0::fmt == 0) epi_int<32, Q0, 32>(u, a.norm, a.q, e0, valid, lane, a.total_groups);
+        if constexpr (Q0::fmt == 0)
+            epi_kron<Q0>(v, a.norm, a.q, a.q.codes + (e0 >> 1), e0 >> 7, valid, valid && g == 0, zbuf + 4 * c + w);
+        __syncthreads();   // operand reads and zero-point bytes done
+        if constexpr (Q0::fmt == 0 && !Q0::sym) {
+            // zero points of groups (2i, 2i + 1) -> one byte: 2 per piece
+            if (w == 0 && lane < 2 * K) {
+                const int pc = lane >> 1, k2 = lane & 1;
+                const uint8_t* zp = zbuf + 4 * pc + 2 * k2;
+                a.q.zeros[((row * n) >> 8) + 2 * pc + k2] = static_cast<uint8_t>(zp[0] | (zp[1] << 4));
+            }
+        }
+        row = next;
+        if (row >= a.rows) break;
     }
 }
 
@@ -765,7 +921,21 @@ int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
 template <int K, bool WROT, class Q0>
 int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
     if (a.k != K || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
-    hipLaunchKernelGGL((kkron<K, WROT, Q0>), dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, s, a);
+    // persistent grid: as many workgroups as the device holds at once
+    static std::atomic<int> slots[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -static_cast<int>(hipErrorInvalidDevice);
+    int cap = slots[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kkron<K, WROT, Q0>, 256, 0) != hipSuccess)
+            return -static_cast<int>(hipErrorInvalidValue);
+        cap = cus * (per > 0 ? per : 1);
+        slots[dev].store(cap, std::memory_order_relaxed);
+    }
+    const int64_t grid = a.rows < cap ? a.rows : cap;
+    hipLaunchKernelGGL((kkron<K, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
