@@ -635,17 +635,19 @@ __device__ __forceinline__ float max_halves(float v) {
 //   XOR-swizzled so that both the staging writes and the operand reads are
 //   free of bank conflicts.
 // Phase 2: v_mfma_f32_32x32x16_bf16 contracts over (u, a) at once, u being
-//   column bits b6..b8: for output bits s and piece c,
-//   Y[c][i + 32 blk + 64 s] = sum_u sum_a H_8[u][s] H_K[a][c] x[a][i + 32 blk + 64 u]
-//   (i = b0..b4, blk = b5). A = 32 columns i by 16 pieces a of x (one u, one
-//   16-byte read per lane), B = +-H_K slice (the sign H_8[u][s] picks the
-//   copy). bf16 times +-1 is exact; the sum is float32. This takes the
-//   base-matrix mix and three of the nine column stages. Wave w owns output
-//   bits (b7, b8) = (w & 1, w >> 1) and all of b0..b6: four tiles (blk, b6).
-//   Lane l then holds piece c = l % 32, b2 = l / 32, and b0, b1, b3, b4, b5
-//   in registers: five butterfly stages, then one across the two half-waves
-//   (v_permlane32_swap) for b2, after which lane l holds the 64 consecutive
-//   columns of piece c with b6 = l / 32.
+//   column bits b7, b8: for output bits s and piece c,
+//   Y[c][b' + 128 s] = sum_u sum_a H_4[u][s] H_K[a][c] x[a][b' + 128 u]
+//   (b' = i + 32 blk + 64 b6 < 128, i = b0..b4, blk = b5). A = 32 columns i
+//   by 16 pieces a of x (one u, one 16-byte read per lane), B = +-H_K slice
+//   (the sign H_4[u][s] picks the copy). bf16 times +-1 is exact; the sum is
+//   float32. This takes the base-matrix mix and two of the nine column stages
+//   (the MFMA does 4 times the useful work of the mix alone, which costs less
+//   than the vector stages it saves only up to about two column bits). Wave w
+//   owns output bits (b7, b8) = (w & 1, w >> 1) and all of b0..b6: four tiles
+//   (blk, b6). Lane l then holds piece c = l % 32, b2 = l / 32, and b0, b1,
+//   b3, b4, b5, b6 in registers: six butterfly stages, then one across the
+//   two half-waves (v_permlane32_swap) for b2, after which lane l holds the
+//   64 consecutive columns of piece c with b6 = l / 32.
 // Epilogue: a group of 128 columns (b0..b6) sits in lanes l and l ^ 32.
 template <int W, int HALVES>
 __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float (&v)[64]) {
@@ -663,7 +665,7 @@ __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float 
             bn[h][p] = x ^ 0x80008000u;
         }
     }
-    // A operand: lane (i, g) element t = x[16 h + 8 g + t][i + 32 blk + 64 u],
+    // A operand: lane (i, g) element t = x[16 h + 8 g + t][i + 32 blk + 64 b6 + 128 u],
     // the 16-byte slot of octet 2 h + g at the swizzled column
     const u32x4_t* ab[2];
 #pragma unroll
@@ -673,23 +675,19 @@ __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float 
     }
     f32x16_t d[4];   // tile blk + 2 b6
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
+        const bool neg = __builtin_popcount(u & W) & 1;
 #pragma unroll
         for (int h = 0; h < HALVES; ++h) {
+            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, neg ? bn[h] : bp[h]);
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[blk][2 * h * 512 + 64 * u]);
-#pragma unroll
-                for (int s0 = 0; s0 < 2; ++s0) {
-                    const int s = s0 + 2 * W;
-                    const bool neg = __builtin_popcount(u & s) & 1;
-                    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, neg ? bn[h] : bp[h]);
-                    f32x16_t& acc = d[blk + 2 * s0];
-                    if (u == 0 && h == 0)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16_t{}, 0, 0, 0);
-                    else
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
-                }
+            for (int t = 0; t < 4; ++t) {
+                const int blk = t & 1, b6 = t >> 1;
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[blk][2 * h * 512 + 64 * b6 + 128 * u]);
+                if (u == 0 && h == 0)
+                    d[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16_t{}, 0, 0, 0);
+                else
+                    d[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, d[t], 0, 0, 0);
             }
         }
     }
@@ -840,7 +838,7 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
         if (stager && next < a.rows) load(next);
         __syncthreads();
 
-        // ---- phase 2: mix on the MFMA, five register stages, one across halves
+        // ---- phase 2: mix on the MFMA, six register stages, one across halves
         float v[64];
         switch (w) {
             case 0: kkron_mix<0, HALVES>(smem, lane, v); break;
@@ -849,7 +847,7 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
             default: kkron_mix<3, HALVES>(smem, lane, v); break;
         }
         // v[16 (blk + 2 b6) + r]: column b0, b1 = r & 3, b3, b4 = r >> 2, b5 = blk; b2 = lane / 32
-        bfly<64, 0x1Fu>(v);
+        bfly<64, 0x3Fu>(v);
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
             float x0 = v[j], x1 = v[j + 32];
