@@ -12,6 +12,10 @@ seeded synthetic input already resident in HBM:
   r3_k     R3 keys (same shape): FWHT 128 + int4 asym per head vector
   weight   W 14336 x 4096 bf16 -> W.H bf16 + MXFP4 + int4 sym g128, one read
 
+Measured only when named in --only (not part of the step): r1_mx32 and
+r4_mx32, the R1 and R4 inputs with a block-32 rotation fused with MXFP4
+(E2M1 codes, one E8M0 scale per block of 32).
+
 The step touches about 2 GB, eight times the 256 MB Infinity Cache, so every
 launch reads its input from HBM.  Timing uses HIP events on the stream the
 kernels are launched on (torch's current stream).  The value is algorithmic
@@ -33,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
 METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
+EXTRA_PARTS = ("r1_mx32", "r4_mx32")     # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -71,6 +76,18 @@ def build_parts(hr, synth, torch, only):
         parts["r1"] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out),
                            bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
         host["r1"] = (x, w.n, 0, [spec], False)
+    # block-32 rotation fused with MXFP4 on the R1 and R4 inputs: measured
+    # only when named in --only (not part of the hot-path step)
+    for name, wn in (("r1_mx32", "r1"), ("r4_mx32", "r4")):
+        if only is not None and name in only:
+            w = W[wn]
+            x = synth.make_inputs(w)
+            spec = hr.QSpec.mxfp4()
+            xg = x.to(dev)
+            out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 32, spec, out=out),
+                               bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
+            host[name] = (x, w.n, 32, [spec], False)
     if want("r4") or want("r4_kron"):
         w = W["r4"]
         x = synth.make_inputs(w)
@@ -174,7 +191,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling)" % ",".join(PARTS))
+    ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling), or of %s (block-32 MXFP4 "
+                         "on the R1 / R4 inputs)" % (",".join(PARTS), ",".join(EXTRA_PARTS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=1.0 / 8)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -198,7 +216,7 @@ def main():
     parts, host = build_parts(hr, synth, torch, only)
     torch.cuda.synchronize()
     print("inputs ready in %.1f s: %s" % (time.perf_counter() - t_gen, ", ".join(parts)), file=sys.stderr, flush=True)
-    names = [p for p in PARTS if p in parts]
+    names = [p for p in PARTS + EXTRA_PARTS if p in parts]
 
     for _ in range(args.warmup):
         for nm in names:

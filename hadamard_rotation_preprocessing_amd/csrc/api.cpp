@@ -231,16 +231,17 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     return HR_OK;
 }
 
-// Specialised bf16 kernels (one wave per 128-, 2048- or 4096-element block;
-// one workgroup per Kronecker row of K x 512) take the call when one is
-// compiled for its exact shape; the generic kernel runs otherwise, or always
-// when HADAROT_FORCE_GENERIC=1.
+// Specialised bf16 kernels (one wave per 128 blocks of 32, per eight rows of
+// 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
+// Kronecker row of K x 512) take the call when one is compiled for its exact
+// shape; the generic kernel runs otherwise, or always when
+// HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
     const hr::RotArgs& a = p.a;
     const char* force = getenv("HADAROT_FORCE_GENERIC");
     const bool generic_only = force && force[0] == '1';
-    if (!generic_only && p.bf16 && a.kron_k == 0 && (a.logb == 7 || a.logb == 11 || a.logb == 12) &&
+    if (!generic_only && p.bf16 && a.kron_k == 0 && (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
         hr::FastArgs f{};

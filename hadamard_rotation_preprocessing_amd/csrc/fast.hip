@@ -887,6 +887,110 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
     }
 }
 
+// ----------------------------------------------------------------- kb32
+// Blocks of 32 (rotation_size 32, the MX block), MXFP4 codes or rotated
+// bf16. v_mfma_f32_16x16x32_bf16 with B = the data: column j is block j of a
+// run of 16 blocks (512 elements) and lane (j, g = lane / 16) holds its
+// elements 8 g .. 8 g + 7, one 16-byte load (so each load instruction reads
+// 1 KiB of consecutive bytes). Two MFMAs (A = the two row halves of H_32,
+// rows permuted) give lane (j, g) the outputs 8 g .. 8 g + 7 of block j:
+// D row 4 g + r of half h is output 8 g + 4 h + r. The whole transform is
+// exact bf16 x +-1 products summed in float32; no butterfly runs on the
+// vector ALU. An MX block's 32 values sit in lanes j, j + 16, j + 32, j + 48.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+struct H32Table {
+    uint32_t w[2][64][4];   // [row half][lane][dword]
+    constexpr H32Table() : w() {
+        for (int h = 0; h < 2; ++h)
+            for (int l = 0; l < 64; ++l)
+                for (int t = 0; t < 8; ++t) {
+                    const int i = l & 15, g = l >> 4;
+                    const int out = 8 * (i >> 2) + 4 * h + (i & 3);   // output position of row i
+                    const int in = 8 * g + t;                         // input position of k = 8 g + t
+                    int p = out & in, par = 0;
+                    while (p) {
+                        par ^= p & 1;
+                        p >>= 1;
+                    }
+                    const uint32_t v = par ? 0xBF80u : 0x3F80u;
+                    w[h][l][t >> 1] |= v << (16 * (t & 1));
+                }
+    }
+};
+__constant__ constexpr H32Table kH32 = H32Table();
+
+// maximum over lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float max_quad16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));   // xor 16
+    return max_halves(v);
+}
+
+template <bool WROT, class Q0>
+__global__ void __launch_bounds__(256) kb32(const FastArgs a) {
+    static_assert(Q0::fmt == 1 || Q0::fmt < 0, "MXFP4 or rotation only");
+    constexpr int CH = 8;                       // runs of 512 elements per wave
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t runs = a.units >> 4;          // units: blocks of 32 (a multiple of 16)
+    const int64_t run0 = wave * CH;
+    if (run0 >= runs) return;
+    const int j = lane & 15, g = lane >> 4;
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);
+    const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
+    const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
+    const uint16_t* src = static_cast<const uint16_t*>(a.x);
+    const int lo = 32 * j + 8 * g;              // the lane's first element within a run
+    u32x4_t raw[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        // a run past the end re-reads the first (finite data, never stored)
+        const int64_t run = run0 + c < runs ? run0 + c : run0;
+        raw[c] = ldg16(src + run * 512 + lo);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, raw[c]);
+        const f32x4v_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, f32x4v_t{}, 0, 0, 0);
+        const f32x4v_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, f32x4v_t{}, 0, 0, 0);
+        float y[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            y[r] = d0[r] * a.norm;
+            y[4 + r] = d1[r] * a.norm;
+        }
+        const bool store = run0 + c < runs;
+        const int64_t e0 = (run0 + c) * 512 + lo;     // first of the lane's 8 elements
+        if constexpr (WROT) {
+            if (store)
+                stg16(static_cast<uint16_t*>(a.y_rot) + e0,
+                      u32x4_t{bf16x2(y[0], y[1]), bf16x2(y[2], y[3]), bf16x2(y[4], y[5]), bf16x2(y[6], y[7])});
+        }
+        if constexpr (Q0::fmt == 1) {
+            float am = fabsf(y[0]);
+#pragma unroll
+            for (int r = 1; r < 8; ++r) am = fmaxf(am, fabsf(y[r]));
+            am = max_quad16(am);
+            const int ex = static_cast<int>((__float_as_uint(am) >> 23) & 0xFFu);
+            const int e = (ex == 0) ? -127 : ex - 129;  // floor(log2 amax) - 2, >= -127
+            uint32_t wc;
+            // 2^-127 is not a normal float: such a block is multiplied by 2^64
+            // and divided by 2^-63 instead, both exact (uniform branch).
+            if (__builtin_amdgcn_ballot_w64(e == -127) == 0) {
+                wc = cvt8_fp4(y, __uint_as_float(static_cast<uint32_t>(e + 127) << 23), 1.0f, false);
+            } else {
+                const bool tiny = e == -127;
+                const float sc = tiny ? __uint_as_float(64u << 23) : __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+                const float pre = tiny ? __uint_as_float(191u << 23) : 1.0f;
+                wc = cvt8_fp4(y, sc, pre, true);
+            }
+            if (store) {
+                *reinterpret_cast<uint32_t*>(a.q[0].codes + (e0 >> 1)) = wc;
+                if (g == 0) static_cast<uint8_t*>(a.q[0].scales)[e0 >> 5] = static_cast<uint8_t>(e + 127);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <class Q>
@@ -912,6 +1016,16 @@ int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
     if (k.logb != 7 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
     const int64_t grid = (a.units + 31) / 32;
     hipLaunchKernelGGL((k128<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 1 : -static_cast<int>(e);
+}
+
+template <bool WROT, class Q0>
+int try_kb32(const FastKey& k, const FastArgs& a, hipStream_t s) {
+    if (k.logb != 5 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1 || (a.units & 15) != 0) return 0;
+    const int64_t waves = ((a.units >> 4) + 7) / 8;
+    const int64_t grid = (waves + 3) / 4;
+    hipLaunchKernelGGL((kb32<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
@@ -994,6 +1108,10 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_k128<true, IA128B>(k, a, s)));
     HR_TRY((try_k128<false, IS128B>(k, a, s)));
     HR_TRY((try_k128<true, IS128B>(k, a, s)));
+    // blocks of 32
+    HR_TRY((try_kb32<false, MX>(k, a, s)));
+    HR_TRY((try_kb32<true, MX>(k, a, s)));
+    HR_TRY((try_kb32<true, QNone>(k, a, s)));
 #undef HR_TRY
     return 0;
 }

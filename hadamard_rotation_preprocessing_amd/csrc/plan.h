@@ -96,7 +96,7 @@ struct KronArgs {
 
 // Compile-time shape of a specialised kernel, matched at dispatch.
 struct FastKey {
-    int logb;                 // 7, 11 or 12
+    int logb;                 // 5, 7, 11 or 12
     int wrot;                 // rotated output written
     int nq;
     int fmt[kMaxQuant], sym[kMaxQuant], logg[kMaxQuant], sdt[kMaxQuant];

@@ -232,6 +232,47 @@ def test_mxfp4_activations(kernel_path, block):
     run_act(x, 4096, block, hr.QSpec.mxfp4(), y_rot=True)
 
 
+# ------------------------------------------- blocks of 32 (MXFP4 activations)
+
+@pytest.mark.parametrize("shape", [(45, 4096), (5, 14336), (7, 1024), (3, 96)],
+                         ids=["r1", "r4", "partial-wave", "not-1024-multiple"])
+@pytest.mark.parametrize("y_rot", [False, True])
+def test_block32_mxfp4(kernel_path, shape, y_rot):
+    """rotation_size 32 (the MX block) fused with MXFP4 on R1/R4-shaped
+    inputs; a row count that leaves a partial wave; and a width that is not a
+    multiple of 1024 elements (served by the generic kernel)."""
+    rows, n = shape
+    if n == 4096:
+        x = synth.make_inputs(synth.WORKLOADS["r1"], tokens=rows)
+    elif n == 14336:
+        x = synth.make_inputs(synth.WORKLOADS["r4"], tokens=rows)
+    else:
+        x = synth.gaussian((rows, n), seed=12000 + n, dtype=torch.bfloat16)
+    run_act(x, n, 32, hr.QSpec.mxfp4(), y_rot=y_rot)
+
+
+def test_block32_degenerate_blocks(kernel_path):
+    n = 1024
+    x = synth.gaussian((6, n), seed=12, dtype=torch.bfloat16)
+    x[0] = 0.0                      # all-zero blocks: E8M0 byte 0, codes 0
+    x[1, :32] = 0.0
+    x[1, 64:96] *= 1e-30
+    x[1, 96:128] *= 1e30
+    x[2, 32:64] = 0.0
+    x[2, 40] = 3.0                  # one-hot block: a flat rotated block
+    out, _ = run_act(x, n, 32, hr.QSpec.mxfp4(), y_rot=True)
+    s = out["scales"].cpu().numpy().reshape(6, n // 32)
+    assert np.all(s[0] == 0) and s[1, 0] == 0
+
+
+@pytest.mark.parametrize("rows", [1, 33, 512])
+def test_block32_rotate(rows):
+    x = synth.gaussian((rows, 2048), seed=13 + rows, dtype=torch.bfloat16)
+    y = hr.rotate(x.to(DEV), 32)
+    torch.cuda.synchronize()
+    check_rotated(to_np64(y), oracle.rotate(x, 2048, 32), "bf16")
+
+
 # ------------------------------------------------------------- special cases
 
 def test_in_place_rotation():
