@@ -1,22 +1,24 @@
 // Specialised bfloat16 kernels for gfx950: every shape parameter is a
-// compile-time constant, one wave owns whole Hadamard blocks, and there is
-// no workgroup barrier.
+// compile-time constant.
 //
 // The Sylvester transform of a block (AutoRound "Rotation Transform",
 // section 1.5: H_{2k} = [[H_k, H_k], [H_k, -H_k]], natural order) is a tensor
 // product of 2x2 butterflies over the index bits, so the bits can be taken in
 // any order and by any mechanism:
-//   * four bits by one MFMA: a lane's four loaded bf16 values are one column
-//     of the B operand of v_mfma_f32_16x16x16_bf16, the A operand is H_16
-//     (entries +-1), so D = H_16 . X transforms four index bits exactly
-//     (bf16 products with +-1 are exact, accumulation is float32) and leaves
-//     every result in the lane and register position of its input;
+//   * bits of exact bf16 inputs by an MFMA: a lane's loaded bf16 values are
+//     B operand columns and A is a +-1 matrix (H_16, H_32, or H_K (x) H_4),
+//     so D = A . X transforms those bits exactly (bf16 products with +-1 are
+//     exact, accumulation is float32);
 //   * bits held in registers: butterflies a +- b;
-//   * lane bits: DPP quad permutations (partner + sign * own);
+//   * lane bits: DPP quad permutations or v_permlane32_swap (partner + sign *
+//     own);
 //   * otherwise an in-wave transpose through a small padded LDS buffer.
 //
-// kwave<LOGB>: one wave per 4096 elements (one 4096 block or two 2048 blocks).
+// kwave<LOGB>: one wave per 4096 elements (one 4096 block or two 2048
+//   blocks), no workgroup barrier.
 // k128: eight rows of 128 elements per wave; no LDS at all.
+// kkron<K>: one workgroup per row of K x 512 (Kronecker form).
+// kb32: 128 blocks of 32 per wave (rotation_size 32, MXFP4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
