@@ -21,8 +21,10 @@ mathematics (H_K . H_K^T = K I), not to the pages' matrices.
 """
 from .hadamard import (  # noqa: F401
     kron_factor,
+    mixing_matrices,
     paley_hadamard,
     rotate,
+    rotate_mixed,
     rotation_matrix,
     sylvester,
     sylvester_entry,

@@ -251,6 +251,49 @@ def rotate(x, n: int, block: int = 0, chunk_rows: int = 2048) -> np.ndarray:
     return y.reshape(*lead, n)
 
 
+def mixing_matrices(n: int, perm=None, in_signs=None, out_signs=None):
+    """Dense factors of the randomised rotations (float64, n x n each):
+
+    * P with P[perm[j], j] = 1, so (x . P)[j] = x[perm[j]] (a gather; the
+      identity when perm is None);
+    * D_in = diag(in_signs) and D_out = diag(out_signs), a negative entry
+      meaning -1 and any other +1 (the identity when None).
+
+    The random Hadamard of the AutoRound page (section 1.5, "Random": H times
+    diag(+-1) over sqrt(N)) is R . D_out; OrbitQuant's RPBH ("Method
+    Conformance": permutation, Rademacher signs, block FWHT, orthonormal
+    scaling) is P . D_in . R.
+    """
+    pm = np.eye(n)
+    if perm is not None:
+        perm = np.asarray(perm, dtype=np.int64).reshape(-1)
+        if perm.shape != (n,) or not np.array_equal(np.sort(perm), np.arange(n)):
+            raise ValueError("perm must be a permutation of 0..n-1")
+        pm = np.zeros((n, n))
+        pm[perm, np.arange(n)] = 1.0
+
+    def diag(s):
+        if s is None:
+            return np.eye(n)
+        s = np.asarray(s).reshape(-1)
+        if s.shape != (n,):
+            raise ValueError("sign vectors must have n entries")
+        return np.diag(np.where(s < 0, -1.0, 1.0))
+
+    return pm, diag(in_signs), diag(out_signs)
+
+
+def rotate_mixed(x, n: int, block: int = 0, perm=None, in_signs=None, out_signs=None) -> np.ndarray:
+    """y = x . P . D_in . R . D_out in float64 (factors as in mixing_matrices,
+    R = rotation_matrix(n, block)), as one dense matrix product per row."""
+    pm, di, do = mixing_matrices(n, perm, in_signs, out_signs)
+    m = pm @ di @ rotation_matrix(n, block) @ do
+    x64 = _as_f64(x)
+    if x64.shape[-1] != n:
+        raise ValueError("last dimension must be n")
+    return (x64.reshape(-1, n) @ m).reshape(x64.shape)
+
+
 def _as_f64(x) -> np.ndarray:
     try:
         import torch

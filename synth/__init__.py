@@ -11,9 +11,11 @@ from .inputs import (  # noqa: F401
     Workload,
     gaussian,
     make_inputs,
+    permutation,
     r1_activations,
     r3_query_key,
     r4_activations,
+    rademacher,
     tiny_activations,
     weight_with_outliers,
 )

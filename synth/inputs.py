@@ -38,6 +38,19 @@ def gaussian(shape, seed: int, dtype=torch.float32, std: float = 1.0) -> torch.T
     return torch.from_numpy(a).to(dtype)
 
 
+def rademacher(n: int, seed: int) -> torch.Tensor:
+    """n independent +-1 signs (int8), as drawn for a random Hadamard or the
+    Rademacher step of RPBH; the draw is an input of both implementations."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.choice(np.array([-1, 1], dtype=np.int8), n))
+
+
+def permutation(n: int, seed: int) -> torch.Tensor:
+    """A uniformly random permutation of 0..n-1 (int32)."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.permutation(n).astype(np.int32))
+
+
 def tiny_activations(seed: int = 1, rows: int = 256, n: int = 128) -> torch.Tensor:
     """Tiny case: rows x n float32, N(0, 1)."""
     return gaussian((rows, n), seed, torch.float32)

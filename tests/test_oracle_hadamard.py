@@ -196,3 +196,62 @@ def test_incoherence_drops_under_rotation():
     y = oracle.rotate(x, 1024)
     assert mu(x) > 50
     assert mu(y) < 2.5 * math.sqrt(2 * math.log(x.size))
+
+
+# ------------------------------------------------ randomised rotations (f2)
+
+@pytest.mark.parametrize("case", ["mixed_h2_rpbh", "mixed_h2_random", "mixed_h4_all"])
+def test_mixed_hand_cases(case):
+    c = GOLDEN[case]
+    n = len(c["x"])
+    y = oracle.rotate_mixed(np.array([c["x"]]), n, 0, c.get("perm"), c.get("in_signs"), c.get("out_signs"))
+    assert np.allclose(y[0], c["y"], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,block", [(64, 0), (64, 16), (48, 0), (256, 32)])
+def test_mixed_identity_reduces_to_plain(n, block):
+    x = np.random.default_rng(n + block).standard_normal((5, n))
+    y = oracle.rotate_mixed(x, n, block, np.arange(n), np.ones(n, np.int8), np.ones(n, np.int8))
+    assert np.allclose(y, oracle.rotate(x, n, block), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,block", [(64, 0), (128, 32), (48, 0), (1024, 64)])
+def test_mixed_orthogonal_and_inverse(n, block):
+    rng = np.random.default_rng(7 * n + block)
+    x = rng.standard_normal((6, n))
+    perm = rng.permutation(n)
+    si = rng.choice([-1, 1], n).astype(np.int8)
+    so = rng.choice([-1, 1], n).astype(np.int8)
+    y = oracle.rotate_mixed(x, n, block, perm, si, so)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    # undo step by step with elementwise operations: out signs, R^T, in signs, scatter
+    z = y * so
+    z = z @ oracle.rotation_matrix(n, block).T
+    z = z * si
+    back = np.empty_like(z)
+    back[:, perm] = z
+    assert np.allclose(back, x, rtol=0, atol=1e-12)
+
+
+def test_mixed_brute_force_tiny():
+    """n = 8, block 4, every factor present: explicit sums over the entries."""
+    rng = np.random.default_rng(3)
+    n, b = 8, 4
+    x = rng.standard_normal(n)
+    perm = rng.permutation(n)
+    si = rng.choice([-1, 1], n)
+    so = rng.choice([-1, 1], n)
+    want = np.zeros(n)
+    for k in range(n):
+        acc = 0.0
+        for j in range(n):
+            if j // b == k // b:
+                acc += si[j] * x[perm[j]] * (-1) ** bin((j % b) & (k % b)).count("1") / 2.0
+        want[k] = so[k] * acc
+    got = oracle.rotate_mixed(x[None], n, b, perm, si, so)[0]
+    assert np.allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_mixed_rejects_non_permutation():
+    with pytest.raises(ValueError):
+        oracle.rotate_mixed(np.zeros((1, 4)), 4, 0, [0, 1, 1, 3])
