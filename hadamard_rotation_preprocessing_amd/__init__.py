@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
     rotate_quantize_act(x, block, qspec, y_rot=False)  -> rotate_quantize_act
     rotate_fuse_weight(w, block, qspecs, w_rot=True)   -> rotate_fuse_weight
     dequant_check(q, qspec, ref=None, ...)             -> dequant_check
+With ``mix=dict(perm=..., in_signs=..., out_signs=...)`` (device tensors,
+int32 / int8 / int8, any subset) the first three call the ``*_mixed`` entry
+points (randomised rotations, hr_mix in the header).
 """
 from __future__ import annotations
 
@@ -93,11 +96,31 @@ def alloc_quant_outputs(rows: int, n: int, spec: QSpec, device) -> dict:
     return out
 
 
-def rotate(x: torch.Tensor, block: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+def _mix(mix: dict | None, n: int):
+    """hr_mix from dict(perm=int32, in_signs=int8, out_signs=int8) of n
+    contiguous device entries each (any subset), or None."""
+    if mix is None:
+        return None
+    want = {"perm": torch.int32, "in_signs": torch.int8, "out_signs": torch.int8}
+    for k, t in mix.items():
+        if k not in want:
+            raise ValueError("unknown mix entry %r" % k)
+        if t is not None and (t.dtype != want[k] or t.numel() != n or not t.is_contiguous()):
+            raise ValueError("mix[%r] must be a contiguous %s tensor of n = %d entries" % (k, want[k], n))
+    m = L.hr_mix(*[(mix[k].data_ptr() if mix.get(k) is not None else None) for k in want])
+    return ctypes.byref(m), m
+
+
+def rotate(x: torch.Tensor, block: int = 0, out: torch.Tensor | None = None,
+           mix: dict | None = None) -> torch.Tensor:
     """y = x . R on the last dimension (block <= 0: full width)."""
     rows, n = _rows_n(x)
     y = torch.empty_like(x) if out is None else out
-    check(lib().hadamard_rotate(_ptr(x), _ptr(y), _dt(x), rows, n, block, _stream(x)))
+    m = _mix(mix, n)
+    if m is None:
+        check(lib().hadamard_rotate(_ptr(x), _ptr(y), _dt(x), rows, n, block, _stream(x)))
+    else:
+        check(lib().hadamard_rotate_mixed(_ptr(x), _ptr(y), _dt(x), rows, n, block, m[0], _stream(x)))
     return y
 
 
@@ -105,7 +128,7 @@ hadamard_rotate = rotate
 
 
 def rotate_quantize_act(x: torch.Tensor, block: int, qspec: QSpec, y_rot: bool = False,
-                        out: dict | None = None) -> dict:
+                        out: dict | None = None, mix: dict | None = None) -> dict:
     """Rotate and quantize activations; returns dict(codes, scales, zeros, y_rot)."""
     rows, n = _rows_n(x)
     o = out if out is not None else alloc_quant_outputs(rows, n, qspec, x.device)
@@ -113,15 +136,19 @@ def rotate_quantize_act(x: torch.Tensor, block: int, qspec: QSpec, y_rot: bool =
         o["y_rot"] = torch.empty_like(x)
     yr = o.get("y_rot") if y_rot else None
     spec = qspec.c()
-    check(lib().rotate_quantize_act(_ptr(x), _dt(x), rows, n, block, ctypes.byref(spec),
-                                    _ptr(o["codes"]), _ptr(o["scales"]), _ptr(o["zeros"]),
-                                    _ptr(yr), _stream(x)))
+    args = (_ptr(x), _dt(x), rows, n, block, ctypes.byref(spec), _ptr(o["codes"]), _ptr(o["scales"]),
+            _ptr(o["zeros"]), _ptr(yr))
+    m = _mix(mix, n)
+    if m is None:
+        check(lib().rotate_quantize_act(*args, _stream(x)))
+    else:
+        check(lib().rotate_quantize_act_mixed(*args, m[0], _stream(x)))
     o["y_rot"] = yr
     return o
 
 
 def rotate_fuse_weight(w: torch.Tensor, block: int, qspecs, w_rot: bool = True,
-                       out: dict | None = None) -> dict:
+                       out: dict | None = None, mix: dict | None = None) -> dict:
     """W' = W . R on in_features plus up to two quantized forms of W' from one
     read; returns dict(w_rot, quant=[dict(codes, scales, zeros), ...])."""
     if w.dim() != 2:
@@ -136,8 +163,12 @@ def rotate_fuse_weight(w: torch.Tensor, block: int, qspecs, w_rot: bool = True,
         *[L.hr_qout(o["codes"].data_ptr(), o["scales"].data_ptr(),
                     o["zeros"].data_ptr() if o["zeros"] is not None else None)
           for o in out["quant"]])
-    check(lib().rotate_fuse_weight(_ptr(w), _dt(w), rows, n, block, _ptr(out["w_rot"]), specs,
-                                   len(qspecs), outs, _stream(w)))
+    args = (_ptr(w), _dt(w), rows, n, block, _ptr(out["w_rot"]), specs, len(qspecs), outs)
+    m = _mix(mix, n)
+    if m is None:
+        check(lib().rotate_fuse_weight(*args, _stream(w)))
+    else:
+        check(lib().rotate_fuse_weight_mixed(*args, m[0], _stream(w)))
     return out
 
 

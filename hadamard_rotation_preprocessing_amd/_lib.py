@@ -17,7 +17,8 @@ HR_Q_INT, HR_Q_MXFP4 = 0, 1
 
 # every exported symbol declared in include/hadarot.h
 EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
-           "dequant_check", "hr_last_error", "hr_kron_order")
+           "dequant_check", "hr_last_error", "hr_kron_order",
+           "hadamard_rotate_mixed", "rotate_quantize_act_mixed", "rotate_fuse_weight_mixed")
 
 
 class hr_qspec(ctypes.Structure):
@@ -29,6 +30,11 @@ class hr_qspec(ctypes.Structure):
 class hr_qout(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p)]
+
+
+class hr_mix(ctypes.Structure):
+    _fields_ = [("perm", ctypes.c_void_p), ("in_signs", ctypes.c_void_p),
+                ("out_signs", ctypes.c_void_p)]
 
 
 class hr_dq_stats(ctypes.Structure):
@@ -70,6 +76,15 @@ def lib() -> ctypes.CDLL:
         L.hr_last_error.restype = ctypes.c_char_p
         L.hr_kron_order.argtypes = [i64, ctypes.POINTER(i32), ctypes.POINTER(i64), vp]
         L.hr_kron_order.restype = ci
+        mp = ctypes.POINTER(hr_mix)
+        L.hadamard_rotate_mixed.argtypes = [vp, vp, ci, i64, i64, i64, mp, vp]
+        L.hadamard_rotate_mixed.restype = ci
+        L.rotate_quantize_act_mixed.argtypes = [vp, ci, i64, i64, i64, ctypes.POINTER(hr_qspec),
+                                                vp, vp, vp, vp, mp, vp]
+        L.rotate_quantize_act_mixed.restype = ci
+        L.rotate_fuse_weight_mixed.argtypes = [vp, ci, i64, i64, i64, vp, ctypes.POINTER(hr_qspec), ci,
+                                               ctypes.POINTER(hr_qout), mp, vp]
+        L.rotate_fuse_weight_mixed.restype = ci
         _lib = L
     return _lib
 

@@ -234,13 +234,13 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
 // Specialised bf16 kernels (one wave per 128 blocks of 32, per eight rows of
 // 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
 // Kronecker row of K x 512) take the call when one is compiled for its exact
-// shape; the generic kernel runs otherwise, or always when
-// HADAROT_FORCE_GENERIC=1.
+// shape; the generic kernel runs otherwise, for every randomised rotation
+// (hr_mix), or always when HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
     const hr::RotArgs& a = p.a;
     const char* force = getenv("HADAROT_FORCE_GENERIC");
-    const bool generic_only = force && force[0] == '1';
+    const bool generic_only = (force && force[0] == '1') || a.perm || a.in_signs || a.out_signs;
     if (!generic_only && p.bf16 && a.kron_k == 0 && (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
@@ -332,6 +332,168 @@ int check_disjoint(const std::vector<Range>& rs) {
     return HR_OK;
 }
 
+// Validated randomised-rotation vectors; ranges for the overlap checks.
+struct Mix {
+    const int32_t* perm = nullptr;
+    const int8_t* in_signs = nullptr;
+    const int8_t* out_signs = nullptr;
+    std::vector<Range> ranges;
+    bool any() const { return perm || in_signs || out_signs; }
+};
+
+int check_mix(const hr_mix* m, int64_t n, Mix* out) {
+    *out = Mix{};
+    if (!m) return HR_OK;
+    out->perm = m->perm;
+    out->in_signs = m->in_signs;
+    out->out_signs = m->out_signs;
+    if (m->perm) {
+        int st = check_ptr(m->perm, "mix->perm", 4);
+        if (st) return st;
+        out->ranges.push_back({"mix->perm", reinterpret_cast<uintptr_t>(m->perm),
+                               reinterpret_cast<uintptr_t>(m->perm) + static_cast<size_t>(n) * 4});
+    }
+    if (m->in_signs)
+        out->ranges.push_back({"mix->in_signs", reinterpret_cast<uintptr_t>(m->in_signs),
+                               reinterpret_cast<uintptr_t>(m->in_signs) + static_cast<size_t>(n)});
+    if (m->out_signs)
+        out->ranges.push_back({"mix->out_signs", reinterpret_cast<uintptr_t>(m->out_signs),
+                               reinterpret_cast<uintptr_t>(m->out_signs) + static_cast<size_t>(n)});
+    return HR_OK;
+}
+
+// The mix vectors are inputs: no output may overlap them.
+int check_mix_outputs(const Mix& mx, const std::vector<Range>& outs) {
+    for (const Range& m : mx.ranges)
+        for (const Range& o : outs)
+            if (o.hi > o.lo && overlap(m, o)) return fail(HR_EINVAL, "output %s overlaps %s", o.name, m.name);
+    return HR_OK;
+}
+
+void apply_mix(const Mix& mx, int64_t n, hr::RotPlan* p) {
+    p->a.perm = mx.perm;
+    p->a.in_signs = mx.in_signs;
+    p->a.out_signs = mx.out_signs;
+    p->a.row_n = n;
+}
+
+int rotate_impl(const void* x, void* y, int dtype, int64_t rows, int64_t n, int64_t block, const hr_mix* mix,
+                void* stream) {
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    st = check_block(n, block, &geo);
+    if (st) return st;
+    Mix mx;
+    if ((st = check_mix(mix, n, &mx))) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(x, "x", 16)) || (st = check_ptr(y, "y", 16))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    Range ry{"y", reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(y) + bytes};
+    if (x != y) {
+        Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
+        if (overlap(rx, ry)) return fail(HR_EINVAL, "y partially overlaps x");
+    } else if (mx.perm) {
+        return fail(HR_EINVAL, "a permuted rotation cannot run in place (y == x)");
+    }
+    if ((st = check_mix_outputs(mx, {ry}))) return st;
+    hr::RotPlan p;
+    st = make_plan(dtype, rows, n, geo, nullptr, 0, &p);
+    if (st) return st;
+    p.a.x = x;
+    p.a.y_rot = y;
+    apply_mix(mx, n, &p);
+    return run(p, stream);
+}
+
+int act_impl(const void* x, int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q, void* codes,
+             void* scales, void* zeros, void* y_rot, const hr_mix* mix, void* stream) {
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    if ((st = check_block(n, block, &geo))) return st;
+    QSpec qs;
+    if ((st = check_qspec(q, n, &qs))) return st;
+    Mix mx;
+    if ((st = check_mix(mix, n, &mx))) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(x, "x", 16))) return st;
+    QBuf b;
+    if ((st = check_qbuffers(qs, rows, n, codes, scales, zeros, "", &b))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
+    std::vector<Range> rs{b.codes, b.scales, b.zeros};
+    if (y_rot) {
+        if ((st = check_ptr(y_rot, "y_rot", 16))) return st;
+        Range ry{"y_rot", reinterpret_cast<uintptr_t>(y_rot), reinterpret_cast<uintptr_t>(y_rot) + bytes};
+        if (y_rot != x && overlap(rx, ry)) return fail(HR_EINVAL, "y_rot partially overlaps x");
+        if (y_rot == x && mx.perm) return fail(HR_EINVAL, "a permuted rotation cannot run in place (y_rot == x)");
+        rs.push_back(ry);
+    }
+    if ((st = check_disjoint(rs))) return st;
+    for (const Range& r : std::vector<Range>{b.codes, b.scales, b.zeros})
+        if (r.hi > r.lo && overlap(r, rx)) return fail(HR_EINVAL, "output %s overlaps x", r.name);
+    if ((st = check_mix_outputs(mx, rs))) return st;
+    hr::RotPlan p;
+    if ((st = make_plan(dtype, rows, n, geo, &qs, 1, &p))) return st;
+    p.a.x = x;
+    p.a.y_rot = y_rot;
+    p.a.q[0].codes = static_cast<uint8_t*>(codes);
+    p.a.q[0].scales = scales;
+    p.a.q[0].zeros = static_cast<uint8_t*>(zeros);
+    apply_mix(mx, n, &p);
+    return run(p, stream);
+}
+
+int weight_impl(const void* w, int dtype, int64_t out_features, int64_t in_features, int64_t block, void* w_rot,
+                const hr_qspec* q, int nq, const hr_qout* outs, const hr_mix* mix, void* stream) {
+    const int64_t rows = out_features, n = in_features;
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    if ((st = check_block(n, block, &geo))) return st;
+    if (nq < 0 || nq > hr::kMaxQuant) return fail(HR_EINVAL, "nq = %d must be 0, 1 or 2", nq);
+    if (nq > 0 && (!q || !outs)) return fail(HR_EINVAL, "q and outs must be given when nq > 0");
+    if (nq == 0 && !w_rot) return fail(HR_EINVAL, "nothing to compute: w_rot is NULL and nq = 0");
+    QSpec qs[hr::kMaxQuant];
+    for (int i = 0; i < nq; ++i)
+        if ((st = check_qspec(&q[i], n, &qs[i]))) return st;
+    Mix mx;
+    if ((st = check_mix(mix, n, &mx))) return st;
+    if (rows == 0) return ok();
+    if ((st = check_ptr(w, "w", 16))) return st;
+    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
+    Range rw{"w", reinterpret_cast<uintptr_t>(w), reinterpret_cast<uintptr_t>(w) + bytes};
+    std::vector<Range> rs;
+    if (w_rot) {
+        if ((st = check_ptr(w_rot, "w_rot", 16))) return st;
+        rs.push_back({"w_rot", reinterpret_cast<uintptr_t>(w_rot), reinterpret_cast<uintptr_t>(w_rot) + bytes});
+    }
+    for (int i = 0; i < nq; ++i) {
+        QBuf b;
+        const char* tag = i == 0 ? "outs[0]." : "outs[1].";
+        if ((st = check_qbuffers(qs[i], rows, n, outs[i].codes, outs[i].scales, outs[i].zeros, tag, &b))) return st;
+        rs.push_back(b.codes);
+        rs.push_back(b.scales);
+        rs.push_back(b.zeros);
+    }
+    if ((st = check_disjoint(rs))) return st;
+    for (const Range& r : rs)
+        if (r.hi > r.lo && overlap(r, rw)) return fail(HR_EINVAL, "output %s overlaps w", r.name);
+    if ((st = check_mix_outputs(mx, rs))) return st;
+    hr::RotPlan p;
+    if ((st = make_plan(dtype, rows, n, geo, qs, nq, &p))) return st;
+    p.a.x = w;
+    p.a.y_rot = w_rot;
+    for (int i = 0; i < nq; ++i) {
+        p.a.q[i].codes = static_cast<uint8_t*>(outs[i].codes);
+        p.a.q[i].scales = outs[i].scales;
+        p.a.q[i].zeros = static_cast<uint8_t*>(outs[i].zeros);
+    }
+    apply_mix(mx, n, &p);
+    return run(p, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,104 +515,33 @@ int hr_kron_order(int64_t n, int32_t* K, int64_t* M, int8_t* hk) {
 }
 
 int hadamard_rotate(const void* x, void* y, int dtype, int64_t rows, int64_t n, int64_t block, void* stream) {
-    int st = check_shape(dtype, rows, n);
-    if (st) return st;
-    Geometry geo;
-    st = check_block(n, block, &geo);
-    if (st) return st;
-    if (rows == 0) return ok();
-    if ((st = check_ptr(x, "x", 16)) || (st = check_ptr(y, "y", 16))) return st;
-    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
-    if (x != y) {
-        Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
-        Range ry{"y", reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(y) + bytes};
-        if (overlap(rx, ry)) return fail(HR_EINVAL, "y partially overlaps x");
-    }
-    hr::RotPlan p;
-    st = make_plan(dtype, rows, n, geo, nullptr, 0, &p);
-    if (st) return st;
-    p.a.x = x;
-    p.a.y_rot = y;
-    return run(p, stream);
+    return rotate_impl(x, y, dtype, rows, n, block, nullptr, stream);
+}
+
+int hadamard_rotate_mixed(const void* x, void* y, int dtype, int64_t rows, int64_t n, int64_t block,
+                          const hr_mix* mix, void* stream) {
+    return rotate_impl(x, y, dtype, rows, n, block, mix, stream);
 }
 
 int rotate_quantize_act(const void* x, int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q,
                         void* codes, void* scales, void* zeros, void* y_rot, void* stream) {
-    int st = check_shape(dtype, rows, n);
-    if (st) return st;
-    Geometry geo;
-    if ((st = check_block(n, block, &geo))) return st;
-    QSpec qs;
-    if ((st = check_qspec(q, n, &qs))) return st;
-    if (rows == 0) return ok();
-    if ((st = check_ptr(x, "x", 16))) return st;
-    QBuf b;
-    if ((st = check_qbuffers(qs, rows, n, codes, scales, zeros, "", &b))) return st;
-    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
-    Range rx{"x", reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + bytes};
-    std::vector<Range> rs{b.codes, b.scales, b.zeros};
-    if (y_rot) {
-        if ((st = check_ptr(y_rot, "y_rot", 16))) return st;
-        Range ry{"y_rot", reinterpret_cast<uintptr_t>(y_rot), reinterpret_cast<uintptr_t>(y_rot) + bytes};
-        if (y_rot != x && overlap(rx, ry)) return fail(HR_EINVAL, "y_rot partially overlaps x");
-        rs.push_back(ry);
-    }
-    if ((st = check_disjoint(rs))) return st;
-    for (const Range& r : std::vector<Range>{b.codes, b.scales, b.zeros})
-        if (r.hi > r.lo && overlap(r, rx)) return fail(HR_EINVAL, "output %s overlaps x", r.name);
-    hr::RotPlan p;
-    if ((st = make_plan(dtype, rows, n, geo, &qs, 1, &p))) return st;
-    p.a.x = x;
-    p.a.y_rot = y_rot;
-    p.a.q[0].codes = static_cast<uint8_t*>(codes);
-    p.a.q[0].scales = scales;
-    p.a.q[0].zeros = static_cast<uint8_t*>(zeros);
-    return run(p, stream);
+    return act_impl(x, dtype, rows, n, block, q, codes, scales, zeros, y_rot, nullptr, stream);
+}
+
+int rotate_quantize_act_mixed(const void* x, int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q,
+                              void* codes, void* scales, void* zeros, void* y_rot, const hr_mix* mix, void* stream) {
+    return act_impl(x, dtype, rows, n, block, q, codes, scales, zeros, y_rot, mix, stream);
 }
 
 int rotate_fuse_weight(const void* w, int dtype, int64_t out_features, int64_t in_features, int64_t block,
                        void* w_rot, const hr_qspec* q, int nq, const hr_qout* outs, void* stream) {
-    const int64_t rows = out_features, n = in_features;
-    int st = check_shape(dtype, rows, n);
-    if (st) return st;
-    Geometry geo;
-    if ((st = check_block(n, block, &geo))) return st;
-    if (nq < 0 || nq > hr::kMaxQuant) return fail(HR_EINVAL, "nq = %d must be 0, 1 or 2", nq);
-    if (nq > 0 && (!q || !outs)) return fail(HR_EINVAL, "q and outs must be given when nq > 0");
-    if (nq == 0 && !w_rot) return fail(HR_EINVAL, "nothing to compute: w_rot is NULL and nq = 0");
-    QSpec qs[hr::kMaxQuant];
-    for (int i = 0; i < nq; ++i)
-        if ((st = check_qspec(&q[i], n, &qs[i]))) return st;
-    if (rows == 0) return ok();
-    if ((st = check_ptr(w, "w", 16))) return st;
-    const size_t bytes = static_cast<size_t>(rows * n) * dtype_size(dtype);
-    Range rw{"w", reinterpret_cast<uintptr_t>(w), reinterpret_cast<uintptr_t>(w) + bytes};
-    std::vector<Range> rs;
-    if (w_rot) {
-        if ((st = check_ptr(w_rot, "w_rot", 16))) return st;
-        rs.push_back({"w_rot", reinterpret_cast<uintptr_t>(w_rot), reinterpret_cast<uintptr_t>(w_rot) + bytes});
-    }
-    for (int i = 0; i < nq; ++i) {
-        QBuf b;
-        const char* tag = i == 0 ? "outs[0]." : "outs[1].";
-        if ((st = check_qbuffers(qs[i], rows, n, outs[i].codes, outs[i].scales, outs[i].zeros, tag, &b))) return st;
-        rs.push_back(b.codes);
-        rs.push_back(b.scales);
-        rs.push_back(b.zeros);
-    }
-    if ((st = check_disjoint(rs))) return st;
-    for (const Range& r : rs)
-        if (r.hi > r.lo && overlap(r, rw)) return fail(HR_EINVAL, "output %s overlaps w", r.name);
-    hr::RotPlan p;
-    if ((st = make_plan(dtype, rows, n, geo, qs, nq, &p))) return st;
-    p.a.x = w;
-    p.a.y_rot = w_rot;
-    for (int i = 0; i < nq; ++i) {
-        p.a.q[i].codes = static_cast<uint8_t*>(outs[i].codes);
-        p.a.q[i].scales = outs[i].scales;
-        p.a.q[i].zeros = static_cast<uint8_t*>(outs[i].zeros);
-    }
-    return run(p, stream);
+    return weight_impl(w, dtype, out_features, in_features, block, w_rot, q, nq, outs, nullptr, stream);
+}
+
+int rotate_fuse_weight_mixed(const void* w, int dtype, int64_t out_features, int64_t in_features, int64_t block,
+                             void* w_rot, const hr_qspec* q, int nq, const hr_qout* outs, const hr_mix* mix,
+                             void* stream) {
+    return weight_impl(w, dtype, out_features, in_features, block, w_rot, q, nq, outs, mix, stream);
 }
 
 int dequant_check(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,

@@ -16,6 +16,11 @@
 //   * Kronecker form (width K * 2^m, section 1.5 of the same page): after the
 //     transform of each length-2^m piece, the K pieces of a row are mixed by
 //     the base matrix: y_c = sum_a H_K[a][c] z_a, one column per thread.
+//   * Randomised rotations (a permutation gather and +-1 signs before the
+//     transform, +-1 signs after it: the random Hadamard H diag(+-1) of the
+//     AutoRound page, section 1.5, and OrbitQuant's RPBH, Method
+//     Conformance) read element by element; with a permutation the loads
+//     are gathers within the row.
 //   * One normalisation multiply, optional store of the rotated tensor, and
 //     up to two fused quantizer epilogues (INT sym/asym groups, MXFP4) that
 //     reduce group statistics across the threads of a group with lane
@@ -83,6 +88,14 @@ __device__ __forceinline__ void load_vals(const void* base, int64_t e0, float (&
             v[1] = d.y;
         }
     }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void* base, int64_t e) {
+    if constexpr (BF16)
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[e]) << 16);
+    else
+        return static_cast<const float*>(base)[e];
 }
 
 template <int E, bool BF16>
@@ -380,8 +393,25 @@ __global__ void __launch_bounds__(1024) rot_kernel(const RotArgs a) {
     const int64_t wg_e0 = static_cast<int64_t>(blockIdx.x) * a.cpw * a.chunk;
 
     float v[E];
+    // randomised rotation: the thread's E elements lie in one row
+    const int64_t col0 = valid && (a.perm || a.in_signs || a.out_signs) ? e0 % a.row_n : 0;
     if (valid) {
-        load_vals<E, BF16>(a.x, e0, v);
+        if (a.perm) {
+            const int64_t rs = e0 - col0;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                int64_t src = a.perm[col0 + j];
+                src = src < 0 ? 0 : (src >= a.row_n ? a.row_n - 1 : src);
+                v[j] = load_one<BF16>(a.x, rs + src);
+            }
+        } else {
+            load_vals<E, BF16>(a.x, e0, v);
+        }
+        if (a.in_signs) {
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                if (a.in_signs[col0 + j] < 0) v[j] = -v[j];
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) v[j] = 0.0f;
@@ -390,6 +420,11 @@ __global__ void __launch_bounds__(1024) rot_kernel(const RotArgs a) {
     if constexpr (KMAX > 0) kron_mix<LOGE, KMAX>(v, lds, tid, a);
 #pragma unroll
     for (int j = 0; j < E; ++j) v[j] *= a.norm;
+    if (a.out_signs && valid) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (a.out_signs[col0 + j] < 0) v[j] = -v[j];
+    }
     if (a.y_rot != nullptr && valid) store_vals<E, BF16>(a.y_rot, e0, v);
     for (int i = 0; i < a.nq; ++i)
         quantize<LOGE>(v, a.q[i], a.total_groups[i], tid, nt, valid, e0, wg_e0, red, zst);

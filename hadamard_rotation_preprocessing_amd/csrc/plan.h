@@ -38,6 +38,13 @@ struct RotArgs {
     // Kronecker base matrix, by output column c: bit a of hk_neg[c] set iff
     // H_K[a][c] == -1, so that y_c = sum_a H_K[a][c] z_a (y = H_K^T z).
     uint64_t hk_neg[kMaxKron];
+    // randomised rotation (all nullable): element j of a row reads
+    // x[perm[j]], is multiplied by in_signs[j] before and out_signs[j] after
+    // the rotation; row_n is the row width n
+    const int32_t* perm;
+    const int8_t* in_signs;
+    const int8_t* out_signs;
+    int64_t row_n;
 };
 
 // Host-side plan.

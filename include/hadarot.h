@@ -185,6 +185,43 @@ int dequant_check(const void* codes, const void* scales, const void* zeros,
                   const hr_qspec* q, int64_t rows, int64_t n, const void* ref,
                   int ref_dtype, float* deq, hr_dq_stats* stats, void* stream);
 
+/*
+ * Randomised rotations: the rotation becomes R' = P . D_in . R . D_out with
+ *   P      the permutation with (x . P)[j] = x[perm[j]] (a gather),
+ *   D_in   diag(in_signs), D_out = diag(out_signs) (+-1 entries),
+ * so y = ((x gathered by perm) * in_signs) . R * out_signs, element j of a
+ * row using perm[j], in_signs[j] and out_signs[j].  The random Hadamard of
+ * the AutoRound page (section 1.5, "Random": H times diag(+-1) over
+ * sqrt(N); section 1.2, random_r1..random_r4) is R . D_out; OrbitQuant's
+ * RPBH (Method Conformance: permutation, Rademacher signs, block FWHT,
+ * orthonormal scaling) is P . D_in . R.  Every member may be NULL (that
+ * factor is the identity).
+ *   perm       device, n int32, 4-byte aligned: a permutation of 0..n-1.
+ *              Entries outside [0, n) are clamped into it (no fault); an
+ *              array that is not a permutation gives an unspecified result.
+ *   in_signs   device, n int8: negative means -1, anything else +1.
+ *   out_signs  device, n int8: likewise.
+ * The vectors are shared by every row and only read.  They may not overlap
+ * an output.  With perm set, the rotation cannot run in place (y == x,
+ * y_rot == x): HR_EINVAL.  Calls with a non-NULL mix run the generic kernel.
+ */
+typedef struct hr_mix {
+    const int32_t* perm;
+    const int8_t* in_signs;
+    const int8_t* out_signs;
+} hr_mix;
+
+/* hadamard_rotate, rotate_quantize_act and rotate_fuse_weight with the
+ * rotation R' of hr_mix; mix == NULL is the plain call. */
+int hadamard_rotate_mixed(const void* x, void* y, int dtype, int64_t rows, int64_t n,
+                          int64_t block, const hr_mix* mix, void* stream);
+int rotate_quantize_act_mixed(const void* x, int dtype, int64_t rows, int64_t n, int64_t block,
+                              const hr_qspec* q, void* codes, void* scales, void* zeros,
+                              void* y_rot, const hr_mix* mix, void* stream);
+int rotate_fuse_weight_mixed(const void* w, int dtype, int64_t out_features, int64_t in_features,
+                             int64_t block, void* w_rot, const hr_qspec* q, int nq,
+                             const hr_qout* outs, const hr_mix* mix, void* stream);
+
 /* Message of the last non-zero status returned on this thread ("" if none). */
 const char* hr_last_error(void);
 

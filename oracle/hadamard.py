@@ -285,13 +285,14 @@ def mixing_matrices(n: int, perm=None, in_signs=None, out_signs=None):
 
 def rotate_mixed(x, n: int, block: int = 0, perm=None, in_signs=None, out_signs=None) -> np.ndarray:
     """y = x . P . D_in . R . D_out in float64 (factors as in mixing_matrices,
-    R = rotation_matrix(n, block)), as one dense matrix product per row."""
+    R = rotation_matrix(n, block)): four dense matrix products, taken left to
+    right on the rows."""
     pm, di, do = mixing_matrices(n, perm, in_signs, out_signs)
-    m = pm @ di @ rotation_matrix(n, block) @ do
     x64 = _as_f64(x)
     if x64.shape[-1] != n:
         raise ValueError("last dimension must be n")
-    return (x64.reshape(-1, n) @ m).reshape(x64.shape)
+    y = x64.reshape(-1, n) @ pm @ di @ rotation_matrix(n, block) @ do
+    return y.reshape(x64.shape)
 
 
 def _as_f64(x) -> np.ndarray:

@@ -145,3 +145,35 @@ def test_kron_order_errors():
     K, M = ctypes.c_int32(), ctypes.c_int64()
     assert lib.hr_kron_order(4096, ctypes.byref(K), ctypes.byref(M), None) == L.HR_EINVAL
     assert lib.hr_kron_order(18, ctypes.byref(K), ctypes.byref(M), None) == L.HR_EUNSUPPORTED
+
+
+def mix(perm=NUL, si=NUL, so=NUL):
+    return ctypes.byref(L.hr_mix(perm, si, so))
+
+
+def test_mixed_validation():
+    lib = L.lib()
+    E = ctypes.c_void_p(P + 6 * (1 << 36))
+    # a permuted rotation cannot run in place
+    assert lib.hadamard_rotate_mixed(A, A, L.HR_BF16, 16, 4096, 0, mix(perm=E), None) == L.HR_EINVAL
+    assert "in place" in msg()
+    # perm must be 4-byte aligned
+    assert lib.hadamard_rotate_mixed(A, B, L.HR_BF16, 16, 4096, 0, mix(perm=ctypes.c_void_p(P + 6 * (1 << 36) + 2)),
+                                     None) == L.HR_EINVAL
+    assert "aligned" in msg()
+    # the vectors are inputs: outputs may not overlap them
+    assert lib.hadamard_rotate_mixed(A, B, L.HR_BF16, 16, 4096, 0, mix(perm=B), None) == L.HR_EINVAL
+    assert "overlaps" in msg()
+    assert lib.rotate_quantize_act_mixed(A, L.HR_BF16, 16, 4096, 0, q(), B, C, NUL, A, mix(perm=E),
+                                         None) == L.HR_EINVAL
+    assert "in place" in msg()
+    assert lib.rotate_quantize_act_mixed(A, L.HR_BF16, 16, 4096, 0, q(), B, C, NUL, NUL, mix(so=B),
+                                         None) == L.HR_EINVAL
+    assert "overlaps" in msg()
+    outs = (L.hr_qout * 1)(L.hr_qout(C.value, D.value, None))
+    assert lib.rotate_fuse_weight_mixed(A, L.HR_BF16, 16, 4096, 0, B, q(), 1, outs, mix(si=B),
+                                        None) == L.HR_EINVAL
+    assert "overlaps" in msg()
+    # invalid shapes are still reported first
+    assert lib.hadamard_rotate_mixed(A, B, L.HR_BF16, 16, 4096, 3, mix(perm=E), None) == L.HR_EINVAL
+    assert "power of two" in msg()

@@ -273,6 +273,81 @@ def test_block32_rotate(rows):
     check_rotated(to_np64(y), oracle.rotate(x, 2048, 32), "bf16")
 
 
+# ------------------------------------------- randomised rotations (hr_mix)
+
+def _mix_cpu(n, seed, perm=False, si=False, so=False):
+    m = {}
+    if perm:
+        m["perm"] = synth.permutation(n, seed)
+    if si:
+        m["in_signs"] = synth.rademacher(n, seed + 1)
+    if so:
+        m["out_signs"] = synth.rademacher(n, seed + 2)
+    return m
+
+
+def _oracle_mixed(x, n, block, m):
+    return oracle.rotate_mixed(x, n, block, m.get("perm"), m.get("in_signs"), m.get("out_signs")).reshape(-1, n)
+
+
+@pytest.mark.parametrize("case", [
+    # (rows, n, block, dtype, perm, in_signs, out_signs, spec)
+    (33, 4096, 0, torch.bfloat16, False, False, True, hr.QSpec("int", 4, 128, True, "bf16")),   # random Hadamard
+    (17, 4096, 0, torch.float32, False, False, True, hr.QSpec("int", 4, 64, False, "f32")),
+    (40, 4096, 256, torch.bfloat16, True, True, False, hr.QSpec("int", 4, 128, False, "bf16")),  # RPBH
+    (40, 4096, 32, torch.bfloat16, True, True, False, hr.QSpec.mxfp4()),                         # RPBH + MX
+    (25, 2048, 512, torch.bfloat16, True, True, True, hr.QSpec("int", 4, 32, True, "bf16")),
+    (19, 96, 0, torch.float32, True, True, True, hr.QSpec("int", 4, 32, True, "f32")),           # Kronecker 12 x 8
+], ids=["random-full-bf16", "random-full-f32", "rpbh-256", "rpbh-32-mxfp4", "all-512", "all-kron96"])
+def test_mixed_rotate_quantize(case):
+    rows, n, block, dt, pm, si, so, spec = case
+    x = synth.gaussian((rows, n), seed=14000 + n + block, dtype=dt)
+    m = _mix_cpu(n, 77 + block, pm, si, so)
+    say("rotate_quantize_act_mixed", rows, n, block, dt, sorted(m), spec)
+    out = hr.rotate_quantize_act(x.to(DEV), block, spec, y_rot=True, mix={k: v.to(DEV) for k, v in m.items()})
+    torch.cuda.synchronize()
+    y = _oracle_mixed(x, n, block, m)
+    rep = Report()
+    kk = oracle.kron_factor(n)[0] if (block <= 0 and n & (n - 1)) else 0
+    check_rotated(to_np64(out["y_rot"]).reshape(-1, n), y, dtname(x), rep)
+    if spec.format == "mxfp4":
+        check_mxfp4(out, y, rep, kron_k=kk)
+    else:
+        check_int(out, y, spec.group_size, spec.sym, spec.scale_dtype, rep, kron_k=kk)
+    say("  ", rep)
+
+
+def test_mixed_rotate_only_and_in_place_signs():
+    n = 1024
+    x = synth.gaussian((65, n), seed=15, dtype=torch.bfloat16)
+    m = _mix_cpu(n, 5, True, True, True)
+    y = hr.rotate(x.to(DEV), 128, mix={k: v.to(DEV) for k, v in m.items()})
+    torch.cuda.synchronize()
+    check_rotated(to_np64(y).reshape(-1, n), _oracle_mixed(x, n, 128, m), "bf16")
+    # signs alone may run in place
+    ms = _mix_cpu(n, 9, False, True, True)
+    xg = x.to(DEV)
+    hr.rotate(xg, 0, out=xg, mix={k: v.to(DEV) for k, v in ms.items()})
+    torch.cuda.synchronize()
+    check_rotated(to_np64(xg).reshape(-1, n), _oracle_mixed(x, n, 0, ms), "bf16")
+
+
+def test_mixed_weight_fusion():
+    """Offline fusion of a random Hadamard, W . H . diag(+-1) / sqrt(N), with
+    MXFP4 and int4 from one read."""
+    rows, n = 96, 4096
+    x = synth.make_inputs(synth.WORKLOADS["weight"], out_features=rows)
+    m = _mix_cpu(n, 21, False, False, True)
+    specs = [hr.QSpec.mxfp4(), hr.QSpec("int", 4, 128, True, "bf16")]
+    out = hr.rotate_fuse_weight(x.to(DEV), 0, specs, mix={k: v.to(DEV) for k, v in m.items()})
+    torch.cuda.synchronize()
+    y = _oracle_mixed(x, n, 0, m)
+    rep = Report()
+    check_rotated(to_np64(out["w_rot"]).reshape(-1, n), y, "bf16", rep)
+    check_mxfp4(out["quant"][0], y, rep)
+    check_int(out["quant"][1], y, 128, True, "bf16", rep)
+
+
 # ------------------------------------------------------------- special cases
 
 def test_in_place_rotation():
