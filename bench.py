@@ -14,7 +14,9 @@ seeded synthetic input already resident in HBM:
 
 Measured only when named in --only (not part of the step): r1_mx32 and
 r4_mx32, the R1 and R4 inputs with a block-32 rotation fused with MXFP4
-(E2M1 codes, one E8M0 scale per block of 32).
+(E2M1 codes, one E8M0 scale per block of 32); r1_random, the R1 part with a
+random Hadamard H diag(+-1); r4_rpbh, the R4 part with RPBH (permutation,
+signs, blocks of 2048).
 
 The step touches about 2 GB, eight times the 256 MB Infinity Cache, so every
 launch reads its input from HBM.  Timing uses HIP events on the stream the
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
 METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
-EXTRA_PARTS = ("r1_mx32", "r4_mx32")     # measured only when named in --only
+EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_random", "r4_rpbh")     # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -88,6 +90,26 @@ def build_parts(hr, synth, torch, only):
             parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 32, spec, out=out),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
             host[name] = (x, w.n, 32, [spec], False)
+    # randomised rotations (hr_mix): the random Hadamard H diag(+-1) on the R1
+    # input, and RPBH (permutation, signs, blocks of 2048) on the R4 input
+    for name, wn, block, pm, si, so in (("r1_random", "r1", 0, False, False, True),
+                                         ("r4_rpbh", "r4", 2048, True, True, False)):
+        if only is not None and name in only:
+            w = W[wn]
+            x = synth.make_inputs(w)
+            spec = hr.QSpec.from_dict(w.qspecs[0])
+            xg = x.to(dev)
+            mix = {}
+            if pm:
+                mix["perm"] = synth.permutation(w.n, 101).to(dev)
+            if si:
+                mix["in_signs"] = synth.rademacher(w.n, 102).to(dev)
+            if so:
+                mix["out_signs"] = synth.rademacher(w.n, 103).to(dev)
+            out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec, block=block, mix=mix:
+                               hr.rotate_quantize_act(xg, block, spec, out=out, mix=mix),
+                               bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
     if want("r4") or want("r4_kron"):
         w = W["r4"]
         x = synth.make_inputs(w)

@@ -234,19 +234,26 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
 // Specialised bf16 kernels (one wave per 128 blocks of 32, per eight rows of
 // 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
 // Kronecker row of K x 512) take the call when one is compiled for its exact
-// shape; the generic kernel runs otherwise, for every randomised rotation
-// (hr_mix), or always when HADAROT_FORCE_GENERIC=1.
+// shape (randomised rotations: signs only, kwave); the generic kernel runs
+// otherwise, or always when HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
     const hr::RotArgs& a = p.a;
     const char* force = getenv("HADAROT_FORCE_GENERIC");
-    const bool generic_only = (force && force[0] == '1') || a.perm || a.in_signs || a.out_signs;
-    if (!generic_only && p.bf16 && a.kron_k == 0 && (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
+    const bool generic_only = force && force[0] == '1';
+    const bool mixed = a.perm || a.in_signs || a.out_signs;
+    // the specialised kernels read the sign vectors 8 and 16 bytes at a time;
+    // a permutation (a gather across the row) runs in the generic kernel
+    const bool signs_aligned =
+        ((reinterpret_cast<uintptr_t>(a.in_signs) | reinterpret_cast<uintptr_t>(a.out_signs)) & 15) == 0;
+    if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned && !a.perm &&
+        (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
         hr::FastArgs f{};
         k.logb = a.logb;
         k.wrot = a.y_rot != nullptr;
+        k.mixed = mixed ? 1 : 0;
         k.nq = a.nq;
         for (int i = 0; i < a.nq; ++i) {
             k.fmt[i] = a.q[i].format;
@@ -260,12 +267,16 @@ int run(const hr::RotPlan& p, void* stream) {
         f.y_rot = a.y_rot;
         f.units = a.total_chunks;
         f.norm = a.norm;
+        f.perm = a.perm;
+        f.in_signs = a.in_signs;
+        f.out_signs = a.out_signs;
+        f.row_blocks = a.row_n / a.chunk;
         const int r = hr::launch_fast(k, f, stream);
         if (r == 1) return ok();
         if (r < 0)
             return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));
     }
-    if (!generic_only && p.bf16 && a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9 && a.nq <= 1) {
+    if (!generic_only && !mixed && p.bf16 && a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9 && a.nq <= 1) {
         hr::FastKey k{};
         hr::KronArgs ka{};
         k.logb = a.logb;
@@ -344,6 +355,8 @@ struct Mix {
 int check_mix(const hr_mix* m, int64_t n, Mix* out) {
     *out = Mix{};
     if (!m) return HR_OK;
+    if ((m->perm || m->in_signs || m->out_signs) && n > INT32_MAX)
+        return fail(HR_EINVAL, "n = %lld: a randomised rotation needs n < 2^31", (long long)n);
     out->perm = m->perm;
     out->in_signs = m->in_signs;
     out->out_signs = m->out_signs;

@@ -374,7 +374,20 @@ struct KW {
 // passes over r gives each lane 64 contiguous elements (L2); bits 3..5 are
 // then register bits and bit 6 is lane bit 0 (DPP).  For 2048-blocks bit 11
 // selects the block and is never mixed.
-template <int LOGB, bool WROT, class Q0, class Q1>
+// Randomised rotation without a permutation (MIXED): element j of a row is
+// multiplied by in_signs[j] before and by out_signs[j] after the transform
+// (the random Hadamard H diag(+-1) of the AutoRound page, section 1.5; the
+// sign step of OrbitQuant's RPBH, Method Conformance); each vector is
+// nullable. Permuted calls run in the generic kernel: a gather inside this
+// kernel (64 scattered 2-byte loads per lane) measured slower than it.
+// Column of element e of block b: (b mod row_blocks) B + e.
+__device__ __forceinline__ uint32_t sign_mask2(uint32_t s, int k) {
+    // bf16 pair (2k, 2k + 1) of the four int8 signs in s: bit 15 and bit 31
+    const uint32_t lo = (s >> (16 * k)) & 0x80u, hi = (s >> (16 * k + 8)) & 0x80u;
+    return (lo << 8) | (hi << 24);
+}
+
+template <int LOGB, bool WROT, class Q0, class Q1, bool MIXED = false>
 __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     static_assert(LOGB == 11 || LOGB == 12, "4096 or 2048 blocks");
     constexpr int E = KW::E, NC = KW::NC, NS = KW::NS, R = KW::R;
@@ -390,12 +403,34 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     const bool hi_ok = BPW == 1 || blk0 + 1 < a.units;
     float* lds = lds_all[wv];
     const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk0 * B;
+    // randomised rotation: column of the wave's (up to) two blocks in their rows
+    int mcol[2] = {0, 0};
+    if constexpr (MIXED) {
+        const int64_t rb = a.row_blocks;
+        const int b0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blk0 % rb));
+        mcol[0] = b0 * B;
+        mcol[1] = b0 + 1 == rb ? 0 : mcol[0] + B;
+    }
 
     // an absent second block re-reads the first (finite data, never stored)
     const int hi_off = hi_ok ? 0 : 512 * (NC / 2);
     u32x4_t raw[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane - (c < NC / 2 ? 0 : hi_off));
+    if constexpr (MIXED) {
+        if (a.in_signs) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int k = ((512 * c) >> LOGB) & (hi_ok ? 1 : 0);   // block of the wave
+                const int col = mcol[k] + ((512 * c + 8 * lane) & (B - 1));
+                const u32x2_t sg = *reinterpret_cast<const u32x2_t*>(a.in_signs + col);
+                raw[c][0] ^= sign_mask2(sg[0], 0);
+                raw[c][1] ^= sign_mask2(sg[0], 1);
+                raw[c][2] ^= sign_mask2(sg[1], 0);
+                raw[c][3] ^= sign_mask2(sg[1], 1);
+            }
+        }
+    }
 
     const bf16x4_t hop = h16_operand(lane);
     float v[E];
@@ -435,6 +470,22 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 
     const bool valid = hi_ok || lane < 32;
     const int64_t e0 = blk0 * B + static_cast<int64_t>(E) * lane;
+    if constexpr (MIXED) {
+        if (a.out_signs) {
+            // the lane's 64 contiguous elements lie in one block
+            const int k = ((E * lane) >> LOGB) & (valid ? 1 : 0);
+            const int col = mcol[k] + ((E * lane) & (B - 1));
+#pragma unroll
+            for (int q4 = 0; q4 < E / 16; ++q4) {
+                const u32x4_t sg = ldg16(a.out_signs + col + 16 * q4);
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const uint32_t bit = ((sg[t >> 2] >> (8 * (t & 3))) & 0x80u) << 24;
+                    y[16 * q4 + t] = __uint_as_float(__float_as_uint(y[16 * q4 + t]) ^ bit);
+                }
+            }
+        }
+    }
     constexpr bool need_y = WROT || Q0::fmt == 1 || Q1::fmt == 1;
     float f = a.norm;
     if constexpr (need_y) {
@@ -1002,20 +1053,22 @@ bool qmatch(const FastKey& k, int i) {
            (Q::fmt == 1 || k.sym[i] == Q::sym);
 }
 
-template <int LOGB, bool WROT, class Q0, class Q1>
+template <int LOGB, bool WROT, class Q0, class Q1, bool MIXED = false>
 int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
-    if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || !qmatch<Q1>(k, 1)) return 0;
+    if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || k.mixed != (MIXED ? 1 : 0) || !qmatch<Q0>(k, 0) ||
+        !qmatch<Q1>(k, 1))
+        return 0;
     constexpr int64_t bpw = 4096 >> LOGB;
     const int64_t waves = (a.units + bpw - 1) / bpw;
     const int64_t grid = (waves + 3) / 4;
-    hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1, MIXED>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
 
 template <bool WROT, class Q0>
 int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
-    if (k.logb != 7 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
+    if (k.mixed || k.logb != 7 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
     const int64_t grid = (a.units + 31) / 32;
     hipLaunchKernelGGL((k128<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
@@ -1024,7 +1077,7 @@ int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
 
 template <bool WROT, class Q0>
 int try_kb32(const FastKey& k, const FastArgs& a, hipStream_t s) {
-    if (k.logb != 5 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1 || (a.units & 15) != 0) return 0;
+    if (k.mixed || k.logb != 5 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1 || (a.units & 15) != 0) return 0;
     const int64_t waves = ((a.units >> 4) + 7) / 8;
     const int64_t grid = (waves + 3) / 4;
     hipLaunchKernelGGL((kb32<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
@@ -1104,6 +1157,14 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<11, false, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, QNone, QNone>(k, a, s)));
+    // randomised rotations (random Hadamard, RPBH)
+    HR_TRY((try_kwave<12, false, IS128B, QNone, true>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA128B, QNone, true>(k, a, s)));
+    HR_TRY((try_kwave<12, true, MX, IS128B, true>(k, a, s)));
+    HR_TRY((try_kwave<12, true, QNone, QNone, true>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IA128B, QNone, true>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS128B, QNone, true>(k, a, s)));
+    HR_TRY((try_kwave<11, true, QNone, QNone, true>(k, a, s)));
     // 128-wide rows
     HR_TRY((try_k128<true, QNone>(k, a, s)));
     HR_TRY((try_k128<false, IA128B>(k, a, s)));

@@ -87,6 +87,12 @@ struct FastArgs {
     int64_t total_groups[kMaxQuant];
     float norm;               // 1/sqrt(block)
     QuantDev q[kMaxQuant];
+    // randomised rotation (kwave only; nullable): as in RotArgs, with
+    // row_blocks = n / block
+    const int32_t* perm;
+    const int8_t* in_signs;
+    const int8_t* out_signs;
+    int64_t row_blocks;
 };
 
 // Arguments of the specialised Kronecker kernel (rows of K * 512 bf16).
@@ -105,6 +111,7 @@ struct KronArgs {
 struct FastKey {
     int logb;                 // 5, 7, 11 or 12
     int wrot;                 // rotated output written
+    int mixed;                // randomised rotation (perm / signs)
     int nq;
     int fmt[kMaxQuant], sym[kMaxQuant], logg[kMaxQuant], sdt[kMaxQuant];
 };

@@ -201,9 +201,11 @@ int dequant_check(const void* codes, const void* scales, const void* zeros,
  *              array that is not a permutation gives an unspecified result.
  *   in_signs   device, n int8: negative means -1, anything else +1.
  *   out_signs  device, n int8: likewise.
- * The vectors are shared by every row and only read.  They may not overlap
+ * n must be below 2^31.  The vectors are shared by every row and only read.  They may not overlap
  * an output.  With perm set, the rotation cannot run in place (y == x,
- * y_rot == x): HR_EINVAL.  Calls with a non-NULL mix run the generic kernel.
+ * y_rot == x): HR_EINVAL.  The specialised kernels take mixed calls of
+ * 2048- and 4096-blocks without a permutation when both sign vectors are
+ * 16-byte aligned (or NULL); other mixed calls run the generic kernel.
  */
 typedef struct hr_mix {
     const int32_t* perm;

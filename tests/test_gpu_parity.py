@@ -298,7 +298,13 @@ def _oracle_mixed(x, n, block, m):
     (40, 4096, 32, torch.bfloat16, True, True, False, hr.QSpec.mxfp4()),                         # RPBH + MX
     (25, 2048, 512, torch.bfloat16, True, True, True, hr.QSpec("int", 4, 32, True, "bf16")),
     (19, 96, 0, torch.float32, True, True, True, hr.QSpec("int", 4, 32, True, "f32")),           # Kronecker 12 x 8
-], ids=["random-full-bf16", "random-full-f32", "rpbh-256", "rpbh-32-mxfp4", "all-512", "all-kron96"])
+    (9, 14336, 2048, torch.bfloat16, True, True, True, hr.QSpec("int", 4, 128, False, "bf16")),   # RPBH, R4 shape
+    (12, 4096, 2048, torch.bfloat16, True, False, False, hr.QSpec("int", 4, 128, True, "bf16")),
+    (7, 4096, 0, torch.bfloat16, True, True, True, hr.QSpec("int", 4, 128, False, "bf16")),
+    (9, 14336, 2048, torch.bfloat16, False, True, True, hr.QSpec("int", 4, 128, False, "bf16")),  # signs, odd blocks
+    (6, 4096, 0, torch.bfloat16, False, True, False, hr.QSpec("int", 4, 128, True, "bf16")),
+], ids=["random-full-bf16", "random-full-f32", "rpbh-256", "rpbh-32-mxfp4", "all-512", "all-kron96",
+        "rpbh-2048-r4", "perm-2048-sym", "all-4096-asym", "signs-2048-r4", "in-signs-4096"])
 def test_mixed_rotate_quantize(case):
     rows, n, block, dt, pm, si, so, spec = case
     x = synth.gaussian((rows, n), seed=14000 + n + block, dtype=dt)
@@ -330,6 +336,24 @@ def test_mixed_rotate_only_and_in_place_signs():
     hr.rotate(xg, 0, out=xg, mix={k: v.to(DEV) for k, v in ms.items()})
     torch.cuda.synchronize()
     check_rotated(to_np64(xg).reshape(-1, n), _oracle_mixed(x, n, 0, ms), "bf16")
+
+
+def test_mixed_rotate_4096_and_unaligned_signs():
+    """Rotation only through the specialised kernel (4096 blocks), and sign
+    vectors that are not 16-byte aligned (served by the generic kernel)."""
+    n = 4096
+    x = synth.gaussian((21, n), seed=16, dtype=torch.bfloat16)
+    m = _mix_cpu(n, 31, True, True, True)
+    y = hr.rotate(x.to(DEV), 0, mix={k: v.to(DEV) for k, v in m.items()})
+    torch.cuda.synchronize()
+    check_rotated(to_np64(y).reshape(-1, n), _oracle_mixed(x, n, 0, m), "bf16")
+    big = torch.zeros(n + 16, dtype=torch.int8, device=DEV)
+    signs = big[1:n + 1]                      # one byte past an aligned base
+    signs.copy_(m["in_signs"].to(DEV))
+    spec = hr.QSpec("int", 4, 128, True, "bf16")
+    out = hr.rotate_quantize_act(x.to(DEV), 0, spec, mix={"in_signs": signs})
+    torch.cuda.synchronize()
+    check_int(out, _oracle_mixed(x, n, 0, {"in_signs": m["in_signs"]}), 128, True, "bf16", Report())
 
 
 def test_mixed_weight_fusion():
