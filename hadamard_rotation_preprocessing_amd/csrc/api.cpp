@@ -234,7 +234,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
 // Specialised bf16 kernels (one wave per 128 blocks of 32, per eight rows of
 // 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
 // Kronecker row of K x 512) take the call when one is compiled for its exact
-// shape (randomised rotations: signs only, kwave); the generic kernel runs
+// shape (randomised rotations: kwave); the generic kernel runs
 // otherwise, or always when HADAROT_FORCE_GENERIC=1.
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
@@ -242,18 +242,17 @@ int run(const hr::RotPlan& p, void* stream) {
     const char* force = getenv("HADAROT_FORCE_GENERIC");
     const bool generic_only = force && force[0] == '1';
     const bool mixed = a.perm || a.in_signs || a.out_signs;
-    // the specialised kernels read the sign vectors 8 and 16 bytes at a time;
-    // a permutation (a gather across the row) runs in the generic kernel
+    // the specialised kernels read the sign vectors 8 and 16 bytes at a time
     const bool signs_aligned =
         ((reinterpret_cast<uintptr_t>(a.in_signs) | reinterpret_cast<uintptr_t>(a.out_signs)) & 15) == 0;
-    if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned && !a.perm &&
+    if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned &&
         (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
         hr::FastArgs f{};
         k.logb = a.logb;
         k.wrot = a.y_rot != nullptr;
-        k.mixed = mixed ? 1 : 0;
+        k.mixed = a.perm ? 2 : (mixed ? 1 : 0);
         k.nq = a.nq;
         for (int i = 0; i < a.nq; ++i) {
             k.fmt[i] = a.q[i].format;

@@ -61,6 +61,9 @@ __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 
 __device__ __forceinline__ u32x4_t ldg16(const void* p) {
     return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
 }
+// Cached loads for the small vectors every row reads again (permutation,
+// signs): a streaming hint would send them back to HBM each time.
+__device__ __forceinline__ u32x4_t ldc16(const void* p) { return *static_cast<const u32x4_t*>(p); }
 // Ordinary stores: a lane's consecutive 16-byte pieces of one cache line are
 // merged in L2 (streaming stores of such partial lines are far slower).
 __device__ __forceinline__ void stg16(void* p, u32x4_t v) { *static_cast<u32x4_t*>(p) = v; }
@@ -374,49 +377,107 @@ struct KW {
 // passes over r gives each lane 64 contiguous elements (L2); bits 3..5 are
 // then register bits and bit 6 is lane bit 0 (DPP).  For 2048-blocks bit 11
 // selects the block and is never mixed.
-// Randomised rotation without a permutation (MIXED): element j of a row is
+// Randomised rotation (MIX > 0): element j of a row reads x[perm[j]] and is
 // multiplied by in_signs[j] before and by out_signs[j] after the transform
-// (the random Hadamard H diag(+-1) of the AutoRound page, section 1.5; the
-// sign step of OrbitQuant's RPBH, Method Conformance); each vector is
-// nullable. Permuted calls run in the generic kernel: a gather inside this
-// kernel (64 scattered 2-byte loads per lane) measured slower than it.
-// Column of element e of block b: (b mod row_blocks) B + e.
+// (the random Hadamard H diag(+-1) of the AutoRound page, section 1.5;
+// OrbitQuant's RPBH, Method Conformance: permutation, Rademacher signs,
+// block FWHT); each vector is nullable. With a permutation (MIX = 2) one
+// workgroup owns a whole row (n <= 16384), stages it in LDS and gathers from
+// there: gathering from global memory (64 scattered 2-byte loads per lane)
+// measured slower than the generic kernel. Column of element e of block b:
+// (b mod row_blocks) B + e.
 __device__ __forceinline__ uint32_t sign_mask2(uint32_t s, int k) {
     // bf16 pair (2k, 2k + 1) of the four int8 signs in s: bit 15 and bit 31
     const uint32_t lo = (s >> (16 * k)) & 0x80u, hi = (s >> (16 * k + 8)) & 0x80u;
     return (lo << 8) | (hi << 24);
 }
 
-template <int LOGB, bool WROT, class Q0, class Q1, bool MIXED = false>
+template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
 __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     static_assert(LOGB == 11 || LOGB == 12, "4096 or 2048 blocks");
     constexpr int E = KW::E, NC = KW::NC, NS = KW::NS, R = KW::R;
     constexpr int B = 1 << LOGB;
     constexpr int BPW = 4096 / B;             // blocks per wave
-    __shared__ float lds_all[4][KW::LDS];
+    constexpr bool MIXED = MIX > 0;           // signs (1) or a permutation and signs (2)
+    constexpr bool PERM = MIX == 2;
+    // permutation: one workgroup per row of n <= 16384, staged in rowbuf, whose
+    // space then holds the waves' transpose buffers
+    constexpr int RB16 = 2 * 4 * KW::LDS > 16384 ? 2 * 4 * KW::LDS : 16384;   // uint16 words
+    __shared__ float lds_all[PERM ? 1 : 4][PERM ? 1 : KW::LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t rowbuf[PERM ? RB16 : 8];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wv;
-    const int64_t blk0 = wave * BPW;
-    if (blk0 >= a.units) return;  // whole wave idle; no barrier follows
-    // with two blocks per wave the second may lie past the end
-    const bool hi_ok = BPW == 1 || blk0 + 1 < a.units;
-    float* lds = lds_all[wv];
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk0 * B;
-    // randomised rotation: column of the wave's (up to) two blocks in their rows
-    int mcol[2] = {0, 0};
-    if constexpr (MIXED) {
-        const int64_t rb = a.row_blocks;
-        const int b0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blk0 % rb));
-        mcol[0] = b0 * B;
-        mcol[1] = b0 + 1 == rb ? 0 : mcol[0] + B;
+    int64_t blk0;
+    bool hi_ok;
+    int mcol[2] = {0, 0};   // randomised rotation: column of the wave's blocks in their rows
+    if constexpr (PERM) {
+        const int rb = static_cast<int>(a.row_blocks);
+        const int n = rb * B;
+        const int64_t row = blockIdx.x;
+        const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * n;
+        // batches of 8 loads in flight per thread
+        const int nq = n / 8, nt = blockDim.x;
+        for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * nt) {
+            u32x4_t t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = q0 + i * nt;
+                t[i] = ldg16(xr + 8 * (q < nq ? q : q0));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = q0 + i * nt;
+                if (q < nq) *reinterpret_cast<u32x4_t*>(rowbuf + 8 * q) = t[i];
+            }
+        }
+        __syncthreads();
+        blk0 = row * rb + wv * BPW;
+        hi_ok = BPW == 1 || wv * BPW + 1 < rb;
+        mcol[0] = wv * BPW * B;
+        mcol[1] = mcol[0] + B;
+    } else {
+        const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+        blk0 = wave * BPW;
+        if (blk0 >= a.units) return;  // whole wave idle; no barrier follows
+        // with two blocks per wave the second may lie past the end
+        hi_ok = BPW == 1 || blk0 + 1 < a.units;
+        if constexpr (MIXED) {
+            const int64_t rb = a.row_blocks;
+            const int b0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blk0 % rb));
+            mcol[0] = b0 * B;
+            mcol[1] = b0 + 1 == rb ? 0 : mcol[0] + B;
+        }
     }
+    float* lds = PERM ? reinterpret_cast<float*>(rowbuf) + wv * KW::LDS : lds_all[wv];
+    const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk0 * B;
 
     // an absent second block re-reads the first (finite data, never stored)
     const int hi_off = hi_ok ? 0 : 512 * (NC / 2);
     u32x4_t raw[NC];
+    if constexpr (PERM) {
+        // gather from the staged row: element j of the row is x[perm[j]]
+        const int nn = static_cast<int>(a.row_blocks) * B;
+        const bool idle = wv * BPW >= a.row_blocks;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane - (c < NC / 2 ? 0 : hi_off));
+        for (int c = 0; c < NC; ++c) {
+            if (idle) break;
+            const int k = ((512 * c) >> LOGB) & (hi_ok ? 1 : 0);
+            const int col = mcol[k] + ((512 * c + 8 * lane) & (B - 1));
+            const u32x4_t p0 = ldc16(a.perm + col), p1 = ldc16(a.perm + col + 4);
+            const int idx[8] = {static_cast<int>(p0[0]), static_cast<int>(p0[1]), static_cast<int>(p0[2]),
+                                static_cast<int>(p0[3]), static_cast<int>(p1[0]), static_cast<int>(p1[1]),
+                                static_cast<int>(p1[2]), static_cast<int>(p1[3])};
+            uint32_t h[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) h[r] = rowbuf[min(max(idx[r], 0), nn - 1)];
+            raw[c] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+        __syncthreads();   // every gather done: rowbuf becomes the transpose buffers
+        if (idle) return;  // whole wave idle; no barrier follows
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane - (c < NC / 2 ? 0 : hi_off));
+    }
     if constexpr (MIXED) {
         if (a.in_signs) {
 #pragma unroll
@@ -477,7 +538,7 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
             const int col = mcol[k] + ((E * lane) & (B - 1));
 #pragma unroll
             for (int q4 = 0; q4 < E / 16; ++q4) {
-                const u32x4_t sg = ldg16(a.out_signs + col + 16 * q4);
+                const u32x4_t sg = ldc16(a.out_signs + col + 16 * q4);
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const uint32_t bit = ((sg[t >> 2] >> (8 * (t & 3))) & 0x80u) << 24;
@@ -1053,15 +1114,23 @@ bool qmatch(const FastKey& k, int i) {
            (Q::fmt == 1 || k.sym[i] == Q::sym);
 }
 
-template <int LOGB, bool WROT, class Q0, class Q1, bool MIXED = false>
+template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
 int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
-    if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || k.mixed != (MIXED ? 1 : 0) || !qmatch<Q0>(k, 0) ||
-        !qmatch<Q1>(k, 1))
+    if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || k.mixed != MIX || !qmatch<Q0>(k, 0) || !qmatch<Q1>(k, 1))
         return 0;
     constexpr int64_t bpw = 4096 >> LOGB;
+    if constexpr (MIX == 2) {
+        // one workgroup per row, its waves owning 4096 elements each
+        if ((a.row_blocks << LOGB) > 16384 || (reinterpret_cast<uintptr_t>(a.perm) & 15) != 0) return 0;
+        const int64_t rows = a.units / a.row_blocks;
+        const int wpr = static_cast<int>((a.row_blocks + bpw - 1) / bpw);
+        hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1, MIX>), dim3(static_cast<unsigned>(rows)), dim3(64 * wpr), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        return e == hipSuccess ? 1 : -static_cast<int>(e);
+    }
     const int64_t waves = (a.units + bpw - 1) / bpw;
     const int64_t grid = (waves + 3) / 4;
-    hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1, MIXED>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1, MIX>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
@@ -1157,14 +1226,20 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<11, false, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, QNone, QNone>(k, a, s)));
-    // randomised rotations (random Hadamard, RPBH)
-    HR_TRY((try_kwave<12, false, IS128B, QNone, true>(k, a, s)));
-    HR_TRY((try_kwave<12, false, IA128B, QNone, true>(k, a, s)));
-    HR_TRY((try_kwave<12, true, MX, IS128B, true>(k, a, s)));
-    HR_TRY((try_kwave<12, true, QNone, QNone, true>(k, a, s)));
-    HR_TRY((try_kwave<11, false, IA128B, QNone, true>(k, a, s)));
-    HR_TRY((try_kwave<11, false, IS128B, QNone, true>(k, a, s)));
-    HR_TRY((try_kwave<11, true, QNone, QNone, true>(k, a, s)));
+    // randomised rotations: signs (random Hadamard), permutation + signs (RPBH)
+    HR_TRY((try_kwave<12, false, IS128B, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA128B, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<12, true, MX, IS128B, 1>(k, a, s)));
+    HR_TRY((try_kwave<12, true, QNone, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IA128B, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS128B, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<11, true, QNone, QNone, 1>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IS128B, QNone, 2>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA128B, QNone, 2>(k, a, s)));
+    HR_TRY((try_kwave<12, true, QNone, QNone, 2>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IA128B, QNone, 2>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS128B, QNone, 2>(k, a, s)));
+    HR_TRY((try_kwave<11, true, QNone, QNone, 2>(k, a, s)));
     // 128-wide rows
     HR_TRY((try_k128<true, QNone>(k, a, s)));
     HR_TRY((try_k128<false, IA128B>(k, a, s)));

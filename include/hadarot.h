@@ -204,8 +204,8 @@ int dequant_check(const void* codes, const void* scales, const void* zeros,
  * n must be below 2^31.  The vectors are shared by every row and only read.  They may not overlap
  * an output.  With perm set, the rotation cannot run in place (y == x,
  * y_rot == x): HR_EINVAL.  The specialised kernels take mixed calls of
- * 2048- and 4096-blocks without a permutation when both sign vectors are
- * 16-byte aligned (or NULL); other mixed calls run the generic kernel.
+ * 2048- and 4096-blocks when the vectors are 16-byte aligned (or NULL) and,
+ * with a permutation, n <= 16384; other mixed calls run the generic kernel.
  */
 typedef struct hr_mix {
     const int32_t* perm;
