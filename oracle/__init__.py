@@ -25,6 +25,7 @@ from .hadamard import (  # noqa: F401
     paley_hadamard,
     rotate,
     rotate_mixed,
+    rotate_out,
     rotation_matrix,
     sylvester,
     sylvester_entry,

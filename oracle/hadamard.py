@@ -295,6 +295,19 @@ def rotate_mixed(x, n: int, block: int = 0, perm=None, in_signs=None, out_signs=
     return y.reshape(x64.shape)
 
 
+def rotate_out(w, out_features: int, block: int = 0) -> np.ndarray:
+    """W' = R^T . W for a weight W [out_features, in_features] (float64): the
+    rotation of the layer's output, absorbed into its weight. For a layer
+    y = x . W^T the rotated output is y . R = x . (R^T W)^T (AutoRound page,
+    section 1.1: R1 fused into the outputs of o_proj / down_proj when
+    online_r1_rotation is False, and R2 on the v_proj output per head of
+    head_dim rows). R = rotation_matrix(out_features, block)."""
+    w64 = _as_f64(w)
+    if w64.ndim != 2 or w64.shape[0] != out_features:
+        raise ValueError("w must be [out_features, in_features]")
+    return rotation_matrix(out_features, block).T @ w64
+
+
 def _as_f64(x) -> np.ndarray:
     try:
         import torch

@@ -255,3 +255,37 @@ def test_mixed_brute_force_tiny():
 def test_mixed_rejects_non_permutation():
     with pytest.raises(ValueError):
         oracle.rotate_mixed(np.zeros((1, 4)), 4, 0, [0, 1, 1, 3])
+
+
+# ------------------------------------------------ output-side weight fusion (f3)
+
+def test_out_fusion_hand_case():
+    c = GOLDEN["out_fusion_h2"]
+    assert np.allclose(oracle.rotate_out(np.array(c["w"]), 2), c["w_rot"], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("out_f,in_f,block", [(64, 24, 0), (256, 40, 32), (128, 16, 128), (48, 8, 0)])
+def test_out_fusion_layer_equivalence(out_f, in_f, block):
+    """For y = x . W^T, the fused weight gives the rotated output:
+    x . (R^T W)^T = (x . W^T) . R, and the rotation of the row side is
+    unchanged by it."""
+    rng = np.random.default_rng(out_f + in_f + block)
+    w = rng.standard_normal((out_f, in_f))
+    x = rng.standard_normal((7, in_f))
+    wr = oracle.rotate_out(w, out_f, block)
+    want = oracle.rotate(x @ w.T, out_f, block)
+    assert np.allclose(x @ wr.T, want, rtol=0, atol=1e-12)
+    # columns keep their norms (orthogonal R)
+    assert np.allclose(np.linalg.norm(wr, axis=0), np.linalg.norm(w, axis=0), rtol=1e-13)
+
+
+def test_out_fusion_brute_force_tiny():
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((8, 3))
+    got = oracle.rotate_out(w, 8, 4)
+    want = np.zeros_like(w)
+    for o in range(8):
+        for i in range(3):
+            want[o, i] = sum(w[r, i] * (-1) ** bin((r % 4) & (o % 4)).count("1") / 2.0
+                             for r in range(8) if r // 4 == o // 4)
+    assert np.allclose(got, want, rtol=0, atol=1e-14)
