@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
 METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
-EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_random", "r4_rpbh")     # measured only when named in --only
+EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_random", "r4_rpbh", "down_out")   # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -110,6 +110,13 @@ def build_parts(hr, synth, torch, only):
             parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec, block=block, mix=mix:
                                hr.rotate_quantize_act(xg, block, spec, out=out, mix=mix),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
+    # output-side fusion W' = R1^T W on down_proj [4096, 14336] (full width
+    # along out_features)
+    if only is not None and "down_out" in only:
+        wd = synth.gaussian((4096, 14336), seed=104, dtype=torch.bfloat16).to(dev)
+        yd = torch.empty_like(wd)
+        parts["down_out"] = dict(fn=lambda wd=wd, yd=yd: hr.rotate_fuse_weight_out(wd, 0, out=yd),
+                                 bytes=wd.numel() * 4, rows=wd.shape[0])
     if want("r4") or want("r4_kron"):
         w = W["r4"]
         x = synth.make_inputs(w)

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     rotate_quantize_act(x, block, qspec, y_rot=False)  -> rotate_quantize_act
     rotate_fuse_weight(w, block, qspecs, w_rot=True)   -> rotate_fuse_weight
     dequant_check(q, qspec, ref=None, ...)             -> dequant_check
+    rotate_fuse_weight_out(w, block=0, out=None)       -> rotate_fuse_weight_out
 With ``mix=dict(perm=..., in_signs=..., out_signs=...)`` (device tensors,
 int32 / int8 / int8, any subset) the first three call the ``*_mixed`` entry
 points (randomised rotations, hr_mix in the header).
@@ -25,7 +26,7 @@ import torch
 from . import _lib as L
 from ._lib import HadarotError, check, lib  # noqa: F401
 
-__all__ = ["QSpec", "rotate", "rotate_quantize_act", "rotate_fuse_weight", "dequant_check",
+__all__ = ["QSpec", "rotate", "rotate_quantize_act", "rotate_fuse_weight", "rotate_fuse_weight_out", "dequant_check",
            "hadamard_rotate", "kron_order", "HadarotError", "alloc_quant_outputs"]
 
 _SCALE_CODES = {"f32": L.HR_F32, "bf16": L.HR_BF16, "e8m0": L.HR_E8M0}
@@ -170,6 +171,17 @@ def rotate_fuse_weight(w: torch.Tensor, block: int, qspecs, w_rot: bool = True,
     else:
         check(lib().rotate_fuse_weight_mixed(*args, m[0], _stream(w)))
     return out
+
+
+def rotate_fuse_weight_out(w: torch.Tensor, block: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W' = R^T . W along out_features (output-side fusion); returns W'."""
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D [out_features, in_features]")
+    if not w.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    y = torch.empty_like(w) if out is None else out
+    check(lib().rotate_fuse_weight_out(_ptr(w), _dt(w), w.shape[0], w.shape[1], block, _ptr(y), _stream(w)))
+    return y
 
 
 def dequant_check(q: dict, qspec: QSpec, rows: int, n: int, ref: torch.Tensor | None = None,

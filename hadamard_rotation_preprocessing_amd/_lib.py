@@ -18,7 +18,8 @@ HR_Q_INT, HR_Q_MXFP4 = 0, 1
 # every exported symbol declared in include/hadarot.h
 EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
            "dequant_check", "hr_last_error", "hr_kron_order",
-           "hadamard_rotate_mixed", "rotate_quantize_act_mixed", "rotate_fuse_weight_mixed")
+           "hadamard_rotate_mixed", "rotate_quantize_act_mixed", "rotate_fuse_weight_mixed",
+           "rotate_fuse_weight_out")
 
 
 class hr_qspec(ctypes.Structure):
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.rotate_fuse_weight_mixed.argtypes = [vp, ci, i64, i64, i64, vp, ctypes.POINTER(hr_qspec), ci,
                                                ctypes.POINTER(hr_qout), mp, vp]
         L.rotate_fuse_weight_mixed.restype = ci
+        L.rotate_fuse_weight_out.argtypes = [vp, ci, i64, i64, i64, vp, vp]
+        L.rotate_fuse_weight_out.restype = ci
         _lib = L
     return _lib
 

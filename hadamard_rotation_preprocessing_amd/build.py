@@ -51,7 +51,7 @@ def build(verbose: bool = True) -> str:
     obj_dir = os.path.join(LIBDIR, "obj")
     os.makedirs(obj_dir, exist_ok=True)
     objs = []
-    sources = [("kernels.hip", True), ("fast.hip", True), ("api.cpp", False), ("paley.cpp", False)]
+    sources = [("kernels.hip", True), ("fast.hip", True), ("colrot.hip", True), ("api.cpp", False), ("paley.cpp", False)]
     for src, device in sources:
         out = os.path.join(obj_dir, src + ".o")
         cmd = [hipcc, "-c"] + (["-x", "hip"] if device else []) + [os.path.join(CSRC, src), "-o", out]

@@ -556,6 +556,54 @@ int rotate_fuse_weight_mixed(const void* w, int dtype, int64_t out_features, int
     return weight_impl(w, dtype, out_features, in_features, block, w_rot, q, nq, outs, mix, stream);
 }
 
+int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64_t in_features, int64_t block,
+                           void* w_rot, void* stream) {
+    int st = check_shape(dtype, out_features, in_features);
+    if (st) return st;
+    if (out_features == 0) return ok();
+    const int64_t b = (block <= 0 || block == out_features) ? out_features : block;
+    if (block > 0 && !is_pow2(block))
+        return fail(HR_EINVAL, "block = %lld is not a power of two", (long long)block);
+    if (out_features % b)
+        return fail(HR_EINVAL, "block %lld does not divide out_features = %lld", (long long)b, (long long)out_features);
+    if (!is_pow2(b) || b < 32 || b > 4096)
+        return fail(HR_EUNSUPPORTED, "output-side rotation needs a power-of-two block of 32..4096 rows (got %lld)",
+                    (long long)b);
+    const int logb = ilog2(b);
+    // tile of b rows x C columns: C >= 8, b C = 2^14 where that allows (or
+    // the largest power of two below it that divides in_features, down to
+    // 2^11 elements)
+    constexpr int kColTileLog = 14;
+    int64_t C = int64_t{1} << (logb + 3 > kColTileLog ? 3 : kColTileLog - logb);
+    while (C > 8 && in_features % C) C >>= 1;
+    if (in_features % C || b * C < 2048)
+        return fail(HR_EUNSUPPORTED, "in_features = %lld must be a multiple of %lld for blocks of %lld rows",
+                    (long long)in_features, (long long)(2048 / b > 8 ? 2048 / b : 8), (long long)b);
+    if ((out_features / b) * (in_features / C) >= (int64_t{1} << 31))
+        return fail(HR_EINVAL, "tensor too large (out_features = %lld, in_features = %lld)", (long long)out_features,
+                    (long long)in_features);
+    if ((st = check_ptr(w, "w", 16)) || (st = check_ptr(w_rot, "w_rot", 16))) return st;
+    const size_t bytes = static_cast<size_t>(out_features * in_features) * dtype_size(dtype);
+    if (w != w_rot) {
+        Range rw{"w", reinterpret_cast<uintptr_t>(w), reinterpret_cast<uintptr_t>(w) + bytes};
+        Range ry{"w_rot", reinterpret_cast<uintptr_t>(w_rot), reinterpret_cast<uintptr_t>(w_rot) + bytes};
+        if (overlap(rw, ry)) return fail(HR_EINVAL, "w_rot partially overlaps w");
+    }
+    hr::ColArgs a{};
+    a.w = w;
+    a.w_rot = w_rot;
+    a.in = in_features;
+    a.row_blocks = out_features / b;
+    a.strips = in_features / C;
+    a.norm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
+    a.logb = logb;
+    a.tb = ilog2(b * C);
+    a.bf16 = dtype == HR_BF16;
+    const int e = hr::launch_colrot(a, stream);
+    if (e != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));
+    return ok();
+}
+
 int dequant_check(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
                   int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* stream) {
     int st = check_shape(HR_F32, rows, n);

@@ -43,8 +43,6 @@ constexpr int kXor2 = 0x4E;        // DPP quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141; // lane i <-> 7 - i within 8
 constexpr int kMirror = 0x140;     // lane i <-> 15 - i within 16
 
-constexpr int kMaxDevices = 64;
-
 template <int FMT, int SYM, int LOGG, int SDT>
 struct QD {
     static constexpr int fmt = FMT, sym = SYM, logg = LOGG, sdt = SDT;

@@ -7,6 +7,9 @@
 
 namespace hr {
 
+// per-device launch caches (persistent grid sizes) hold this many devices
+constexpr int kMaxDevices = 64;
+
 constexpr int kMaxQuant = 2;
 constexpr int kMaxKron = 64;   // largest Kronecker base order handled on the GPU
 
@@ -116,7 +119,21 @@ struct FastKey {
     int fmt[kMaxQuant], sym[kMaxQuant], logg[kMaxQuant], sdt[kMaxQuant];
 };
 
+// Output-side weight fusion (colrot.hip): W' = R^T W along out_features.
+struct ColArgs {
+    const void* w;
+    void* w_rot;
+    int64_t in;               // in_features (row length)
+    int64_t row_blocks;       // out_features / b
+    int64_t strips;           // in_features / C
+    float norm;               // 1 / sqrt(b)
+    int32_t logb;             // b = 2^logb, 5..12
+    int32_t tb;               // tile of 2^tb elements (b C), 11..15
+    int32_t bf16;
+};
+
 int launch_rotate(const RotPlan& p, void* stream);        // returns hipError_t
+int launch_colrot(const ColArgs& a, void* stream);        // returns hipError_t
 // Launches a specialised kernel if one matches `k`: returns 1 if launched,
 // 0 if none matches, or a negative hipError_t on a launch error.
 int launch_fast(const FastKey& k, const FastArgs& a, void* stream);

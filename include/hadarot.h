@@ -166,6 +166,27 @@ int rotate_fuse_weight(const void* w, int dtype, int64_t out_features, int64_t i
                        const hr_qout* outs, void* stream);
 
 /*
+ * Output-side weight fusion W' = R^T . W along out_features (AutoRound page,
+ * section 1.1: R1 fused into the outputs of o_proj / down_proj / embed when
+ * online_r1_rotation is False, and R2 per head of head_dim rows on the v_proj
+ * output).  For a layer y = x . W^T this gives y . R = x . W'^T.
+ *   w      device, [out_features, in_features] of `dtype`.
+ *   w_rot  device, the same shape and dtype; may equal w (in place), may not
+ *          partially overlap it.
+ *   block  > 0: R = blockdiag(H_block) / sqrt(block) over groups of `block`
+ *          consecutive rows; <= 0 or == out_features: full width.  The block
+ *          must be a power of two dividing out_features with 32 <= block <=
+ *          4096, and in_features a multiple of max(8, 2048 / block):
+ *          HR_EUNSUPPORTED otherwise (including full width on a
+ *          non-power-of-two out_features).
+ * out_features == 0 is an empty weight (HR_OK, nothing enqueued).
+ * Output is rounded to `dtype` (nearest even).  Quantize W' along
+ * in_features afterwards with rotate_fuse_weight and block = 1 (H_1 = 1).
+ */
+int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64_t in_features,
+                           int64_t block, void* w_rot, void* stream);
+
+/*
  * Dequantize packed codes (orbitquant 0.2.0, "Packed Runtime": an explicit
  * dequantized reference mode for numerical debugging):
  *   INT symmetric q * s; INT asymmetric (q - z) * s; MXFP4 E2M1 * 2^e.

@@ -177,3 +177,20 @@ def test_mixed_validation():
     # invalid shapes are still reported first
     assert lib.hadamard_rotate_mixed(A, B, L.HR_BF16, 16, 4096, 3, mix(perm=E), None) == L.HR_EINVAL
     assert "power of two" in msg()
+
+
+def test_weight_out_validation():
+    lib = L.lib()
+    f = lib.rotate_fuse_weight_out
+    assert f(A, L.HR_BF16, 4096, 4096, 3, B, None) == L.HR_EINVAL and "power of two" in msg()
+    assert f(A, L.HR_BF16, 4096, 4096, 16, B, None) == L.HR_EUNSUPPORTED and "32..4096" in msg()
+    assert f(A, L.HR_BF16, 8192, 4096, 0, B, None) == L.HR_EUNSUPPORTED
+    assert f(A, L.HR_BF16, 96, 4096, 0, B, None) == L.HR_EUNSUPPORTED
+    assert f(A, L.HR_BF16, 4096, 4096, 8192, B, None) == L.HR_EINVAL and "divide" in msg()
+    assert f(A, L.HR_BF16, 4096, 100, 0, B, None) == L.HR_EUNSUPPORTED and "multiple" in msg()
+    assert f(A, L.HR_BF16, 64, 32, 32, B, None) == L.HR_EUNSUPPORTED       # 32 x 32 < one tile of 2048
+    assert f(A, 5, 4096, 4096, 0, B, None) == L.HR_EINVAL and "dtype" in msg()
+    assert f(A, L.HR_BF16, 4096, 4096, 0, ctypes.c_void_p(A.value + 64), None) == L.HR_EINVAL
+    assert "overlaps" in msg()
+    assert f(NUL, L.HR_BF16, 4096, 4096, 0, B, None) == L.HR_EINVAL
+    assert f(NUL, L.HR_BF16, 0, 4096, 0, NUL, None) == L.HR_OK

@@ -372,6 +372,44 @@ def test_mixed_weight_fusion():
     check_int(out["quant"][1], y, 128, True, "bf16", rep)
 
 
+# ------------------------------------------- output-side weight fusion (R^T W)
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 0), (4096, 14336, 0), (4096, 4096, 128), (2048, 1024, 256),
+                                   (64, 64, 32), (1024, 96, 64), (4096, 6184, 0), (2048, 2056, 1024)],
+                         ids=["o_proj-R1", "down_proj-R1", "v_proj-R2", "b256", "b32-small", "f32-b64",
+                              "tiles-not-8k", "b1024-ragged"])
+def test_weight_out_fusion(shape):
+    out_f, in_f, block = shape
+    dt = torch.float32 if in_f == 96 else torch.bfloat16
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=out_f, in_features=in_f).to(dt)
+    say("rotate_fuse_weight_out", out_f, in_f, block, dt)
+    wr = hr.rotate_fuse_weight_out(w.to(DEV), block)
+    torch.cuda.synchronize()
+    cols = np.unique(np.random.default_rng(out_f + in_f).choice(in_f, size=min(in_f, 96), replace=False))
+    ref = oracle.rotate_out(w[:, torch.as_tensor(cols)], out_f, block)
+    got = to_np64(wr)[:, cols]
+    check_rotated(got.T.copy(), ref.T.copy(), dtname(w))
+
+
+def test_weight_out_in_place_and_layer_equivalence():
+    """In place, and the fused weight reproduces the rotated layer output:
+    x . W'^T against (x . W^T) . R on the GPU-rounded weight."""
+    out_f, in_f = 1024, 512
+    w = synth.gaussian((out_f, in_f), seed=17, dtype=torch.float32)
+    wg = w.to(DEV)
+    hr.rotate_fuse_weight_out(wg, 0, out=wg)
+    torch.cuda.synchronize()
+    x = np.random.default_rng(5).standard_normal((9, in_f))
+    lhs = x @ to_np64(wg).T
+    rhs = oracle.rotate(x @ to_np64(w).T, out_f)
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-4 * np.abs(rhs).max())
+    # W' then quantized along in_features with the identity rotation (block 1)
+    spec = hr.QSpec("int", 4, 128, True, "f32")
+    o = hr.rotate_fuse_weight(wg, 1, [spec], w_rot=False)["quant"][0]
+    torch.cuda.synchronize()
+    check_int(o, to_np64(wg), 128, True, "f32", Report())
+
+
 # ------------------------------------------------------------- special cases
 
 def test_in_place_rotation():
