@@ -6,8 +6,8 @@ GPU library computes, from the definitions on the pages:
 * the rotation is the explicit dense product y = x . R with R built as a
   matrix (Sylvester Hadamard, block-diagonal Hadamard, or a Kronecker product
   of a Paley base matrix and a Sylvester matrix), normalised to be orthogonal;
-* the quantizers (round-to-nearest integer groups, MXFP4) are evaluated
-  element by element with numpy's round-half-to-even.
+* the quantizers (round-to-nearest integer groups, MXFP4, NVFP4) are
+  evaluated element by element with numpy's round-half-to-even.
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  It shares no code with the HIP library and
@@ -17,7 +17,10 @@ Parity status of each function is stated in its docstring.  One part is
 *parity unpinned* against the pages: the Paley base matrices used for widths
 that are not a power of two are this project's own construction (the pages'
 table of known matrices is not available); they are pinned to the
-mathematics (H_K . H_K^T = K I), not to the pages' matrices.
+mathematics (H_K . H_K^T = K I), not to the pages' matrices.  NVFP4 is
+named on the pages without its encoding: its reading (module text of
+``quant``) is pinned to the public format through PyTorch's float8_e4m3fn
+conversion and to hand-derived cases, not to the pages.
 """
 from .hadamard import (  # noqa: F401
     kron_factor,
@@ -36,9 +39,13 @@ from .quant import (  # noqa: F401
     bf16_round,
     dequant_int,
     dequant_mxfp4,
+    dequant_nvfp4,
     e2m1_round,
+    e4m3_decode,
+    e4m3_encode,
     fp32_round,
     mxfp4_quant,
+    nvfp4_quant,
     pack_nibbles,
     round_scale,
     rtn_codes,

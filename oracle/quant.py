@@ -28,6 +28,15 @@ and stated here:
   saturating at +-6; the 4-bit code is sign << 3 | index with
   index 0..7 <-> {0, 0.5, 1, 1.5, 2, 3, 4, 6}; the sign bit is set iff y < 0
   (a negative value that rounds to zero keeps its sign, code 0x8);
+* NVFP4 (named on the AutoRound page, sections 2 and 2.1, with rotation
+  blocks of 16; its encoding is not on the pages, so this reading is the
+  public two-level one): blocks of 16 consecutive elements; a float32 tensor
+  scale g > 0 chosen by the caller (1 for a single-level scale); the block
+  scale byte is E4M3 (OCP e4m3fn: bias 7, 3 mantissa bits, subnormals down
+  to 2^-9, no infinities) of d = amax / (6 g), round to nearest even,
+  saturating at 448; every element is E2M1 of y / (E4M3(d) g) with the
+  MXFP4 rounding rules; a block whose scale byte is 0 stores code 0 for
+  every element;
 * rne is round half to even (numpy.rint);
 * codes are packed two per byte, element 2j in the low nibble; symmetric
   codes are stored as two's complement nibbles; zero points are packed the
@@ -189,6 +198,73 @@ def dequant_mxfp4(codes, e8m0, group_size: int = 32) -> np.ndarray:
     val = np.where(c & 8, -mag, mag).reshape(rows, n // group_size, group_size)
     e = np.asarray(e8m0, dtype=np.int64) - 127
     return np.ldexp(val, e[..., None]).reshape(rows, n)
+
+
+# -------------------------------------------------------------------- NVFP4
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(byte) -> np.ndarray:
+    """Value of E4M3 (e4m3fn) bytes: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 is subnormal (m / 8 * 2^-6); 0x7F / 0xFF
+    are NaN."""
+    b = np.asarray(byte, dtype=np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    ef = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(ef == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, ef - 7))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 byte of non-negative values: nearest representable magnitude,
+    ties to the even mantissa, saturating at 448 (so no NaN is produced)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(v < 0) or np.any(np.isnan(v)):
+        raise ValueError("E4M3 scales are encoded from non-negative values")
+    a = np.minimum(v, E4M3_MAX)
+    # exponent of the binade, clamped to the subnormal binade below 2^-6
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f 2^ex, 0.5 <= f < 1
+    e = np.maximum(ex.astype(np.int64) - 1, -6)        # floor(log2 a), >= -6
+    q = np.rint(np.ldexp(a, 3 - e))                    # units of 2^(e - 3), ties to even
+    # q in 8..16 for normals (16 carries into the next binade), 0..8 subnormal
+    carry = q >= 16
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, q / 2, q)
+    normal = q >= 8
+    ef = np.where(normal, e + 7, 0)
+    mant = np.where(normal, q - 8, q).astype(np.int64)
+    return np.where(a > 0, (ef.astype(np.int64) << 3) | mant, 0).astype(np.int64)
+
+
+def nvfp4_quant(y, group_size: int = 16, tensor_scale: float = 1.0) -> QuantResult:
+    """NVFP4 quantization of y [..., n] (see module text): E4M3 block scale
+    bytes of amax / (6 g), E2M1 codes of y / (E4M3 g)."""
+    if not tensor_scale > 0 or not np.isfinite(tensor_scale):
+        raise ValueError("tensor scale must be positive and finite")
+    yg = _groups(y, group_size)
+    rows = yg.shape[0]
+    n = yg.shape[1] * group_size
+    g = float(tensor_scale)
+    amax = np.abs(yg).max(axis=-1)
+    d = amax / (6.0 * g)
+    byte = e4m3_encode(d)
+    s = e4m3_decode(byte) * g
+    safe = np.where(s > 0, s, 1.0)
+    pre = np.where(s[..., None] > 0, yg / safe[..., None], 0.0)
+    codes = np.where(s[..., None] > 0, e2m1_round(pre), 0)
+    return QuantResult(codes.reshape(rows, n), byte, None, d, pre.reshape(rows, n))
+
+
+def dequant_nvfp4(codes, e4m3, group_size: int = 16, tensor_scale: float = 1.0) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    rows, n = c.shape
+    mag = E2M1_VALUES[c & 7]
+    val = np.where(c & 8, -mag, mag).reshape(rows, n // group_size, group_size)
+    s = e4m3_decode(e4m3) * float(tensor_scale)
+    return (val * s[..., None]).reshape(rows, n)
 
 
 # ------------------------------------------------------------------ packing

@@ -5,7 +5,10 @@ search in exact rational arithmetic (fractions.Fraction) on tiny groups, the
 round-off bounds from the QuIP note ("The math, slowly": per-element error
 within half a step, mean square a twelfth of a step squared), torch's
 float32 -> bfloat16 conversion as a library cross-check for the bfloat16
-rounding, and the MXFP4 scale bracket amax / 2^e in [4, 8).
+rounding, and the MXFP4 scale bracket amax / 2^e in [4, 8).  NVFP4: the E4M3
+scale byte against PyTorch's float8_e4m3fn conversion (an independent
+implementation of the public format), hand-worked blocks, and exact brute
+force over every E4M3 and E2M1 value.
 """
 import json
 import math
@@ -235,6 +238,111 @@ def test_mxfp4_brute_force_groups():
 def test_mxfp4_zero_group():
     r = oracle.mxfp4_quant(np.zeros((1, 64)), 32)
     assert r.scales.tolist() == [[0, 0]] and np.all(r.codes == 0)
+
+
+# -------------------------------------------------------------------- NVFP4
+
+def test_e4m3_closed_forms():
+    c = GOLDEN["e4m3_values"]
+    got = oracle.e4m3_decode(np.array(c["bytes"]))
+    assert got.tolist() == c["values"]
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+    assert oracle.e4m3_decode(np.array([0x80 | 56]))[0] == -1.0
+    assert oracle.e4m3_encode(np.array(c["values"])).tolist() == c["bytes"]
+
+
+def _e4m3_grid():
+    """Every finite non-negative E4M3 value by byte, from torch's own decoder."""
+    b = torch.arange(0, 127, dtype=torch.uint8)
+    return b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_torch():
+    assert np.array_equal(oracle.e4m3_decode(np.arange(127)), _e4m3_grid())
+
+
+def test_e4m3_encode_matches_torch():
+    """PyTorch's float32 -> float8_e4m3fn conversion is an independent
+    implementation of the same rounding (nearest, ties to even); it is
+    compared below 464, above which it gives NaN where the oracle saturates."""
+    grid = _e4m3_grid()
+    mids = (grid[1:] + grid[:-1]) / 2                # every tie, exact in float32
+    rng = np.random.default_rng(11)
+    rand = np.exp2(rng.uniform(-13, np.log2(463.9), 20000))
+    v = np.concatenate([grid, mids, rand, [464.0]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    assert np.array_equal(oracle.e4m3_encode(v.astype(np.float64)), ref)
+
+
+def test_e4m3_saturates_and_rejects_negative():
+    assert oracle.e4m3_encode(np.array([448.0, 464.0, 465.0, 1e30, np.inf])).tolist() == [126] * 5
+    with pytest.raises(ValueError):
+        oracle.e4m3_encode(np.array([-1.0]))
+
+
+def _brute_e4m3(d: Fraction) -> int:
+    """Nearest E4M3 byte to d >= 0 in exact arithmetic, ties to the even
+    mantissa, saturating at 448."""
+    grid = _e4m3_grid()
+    best = None
+    for byte, val in enumerate(grid):
+        key = (abs(d - Fraction(float(val))), byte & 1)
+        if best is None or key < best[0]:
+            best = (key, byte)
+    return best[1]
+
+
+def test_nvfp4_hand_cases():
+    for c in GOLDEN["nvfp4_cases"]["cases"]:
+        y = np.array(c["y"] + [0.0] * (16 - len(c["y"])))
+        r = oracle.nvfp4_quant(y[None, :], 16, c["g"])
+        assert r.scales[0, 0] == c["byte"], c["note"]
+        assert r.codes[0, :len(c["codes"])].tolist() == c["codes"], c["note"]
+        if c["byte"]:
+            assert np.all(r.codes[0, len(c["codes"]):] == 0)
+        deq = oracle.dequant_nvfp4(r.codes, r.scales, 16, c["g"])[0, :len(c["values"])]
+        assert deq.tolist() == c["values"], c["note"]
+
+
+def test_nvfp4_brute_force_blocks():
+    rng = np.random.default_rng(12)
+    for trial in range(80):
+        y = rng.standard_normal(16) * 10.0 ** rng.integers(-4, 4)
+        g = float(np.float32(2.0 ** rng.uniform(-6, 3))) if trial % 2 else 1.0
+        r = oracle.nvfp4_quant(y[None, :], 16, g)
+        d = Fraction(float(np.abs(y).max())) / (6 * Fraction(g))
+        byte = _brute_e4m3(d)
+        assert r.scales[0, 0] == byte
+        s = Fraction(float(_e4m3_grid()[byte])) * Fraction(g)
+        for k in range(16):
+            want = _brute_e2m1(float(Fraction(float(y[k])) / s)) if s else 0
+            assert r.codes[0, k] == want
+
+
+def test_nvfp4_error_bound():
+    """Each element dequantizes within half of the local E2M1 spacing times
+    the block scale, unless y / s is beyond 6 (saturated)."""
+    rng = np.random.default_rng(13)
+    y = rng.standard_normal((64, 256)) * np.exp2(rng.integers(-8, 8, (64, 1)))
+    r = oracle.nvfp4_quant(y, 16, 0.5)
+    deq = oracle.dequant_nvfp4(r.codes, r.scales, 16, 0.5)
+    s = np.repeat(oracle.e4m3_decode(r.scales) * 0.5, 16, axis=1)
+    a = np.abs(y) / s
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+    ok = a <= 6
+    assert np.all(np.abs(deq - y)[ok] <= (half * s)[ok] * (1 + 1e-12))
+    # the block maximum lands on a code near 6: its scale is amax / 6 rounded
+    # to 4 significant bits, within 1/16 relative
+    amax_codes = np.abs(y).reshape(64, 16, 16).argmax(-1)
+    top = np.take_along_axis(r.codes.reshape(64, 16, 16), amax_codes[..., None], -1)[..., 0] & 7
+    assert np.all(top >= 6)
+
+
+def test_nvfp4_zero_and_invalid():
+    r = oracle.nvfp4_quant(np.zeros((1, 32)), 16)
+    assert r.scales.tolist() == [[0, 0]] and np.all(r.codes == 0)
+    with pytest.raises(ValueError):
+        oracle.nvfp4_quant(np.zeros((1, 16)), 16, 0.0)
 
 
 # ----------------------------------------------------------------- packing
