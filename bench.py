@@ -14,7 +14,9 @@ seeded synthetic input already resident in HBM:
 
 Measured only when named in --only (not part of the step): r1_mx32 and
 r4_mx32, the R1 and R4 inputs with a block-32 rotation fused with MXFP4
-(E2M1 codes, one E8M0 scale per block of 32); r1_random, the R1 part with a
+(E2M1 codes, one E8M0 scale per block of 32); r1_nv16 and r4_nv16, the same
+inputs with a block-16 rotation fused with NVFP4 (one E4M3 scale per block
+of 16); r1_random, the R1 part with a
 random Hadamard H diag(+-1); r4_rpbh, the R4 part with RPBH (permutation,
 signs, blocks of 2048); down_out, the output-side fusion R1^T W on down_proj
 [4096, 14336].
@@ -42,7 +44,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD published peak
 METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
-EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_random", "r4_rpbh", "down_out")   # measured only when named in --only
+EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_nv16", "r4_nv16", "r1_random", "r4_rpbh",
+               "down_out")   # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -93,6 +96,17 @@ def build_parts(hr, synth, torch, only):
             parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 32, spec, out=out),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
             host[name] = (x, w.n, 32, [spec], False)
+    # block-16 rotation fused with NVFP4 (E4M3 block scales, unit tensor
+    # scale) on the R1 and R4 inputs
+    for name, wn in (("r1_nv16", "r1"), ("r4_nv16", "r4")):
+        if only is not None and name in only:
+            w = W[wn]
+            x = synth.make_inputs(w)
+            spec = hr.QSpec.nvfp4()
+            xg = x.to(dev)
+            out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
+            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 16, spec, out=out),
+                               bytes=x.numel() * 2 + x.numel() // 2 + x.numel() // 16, rows=x.shape[0])
     # randomised rotations (hr_mix): the random Hadamard H diag(+-1) on the R1
     # input, and RPBH (permutation, signs, blocks of 2048) on the R4 input
     for name, wn, block, pm, si, so in (("r1_random", "r1", 0, False, False, True),

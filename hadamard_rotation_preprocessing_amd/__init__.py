@@ -29,32 +29,39 @@ from ._lib import HadarotError, check, lib  # noqa: F401
 __all__ = ["QSpec", "rotate", "rotate_quantize_act", "rotate_fuse_weight", "rotate_fuse_weight_out", "dequant_check",
            "hadamard_rotate", "kron_order", "HadarotError", "alloc_quant_outputs"]
 
-_SCALE_CODES = {"f32": L.HR_F32, "bf16": L.HR_BF16, "e8m0": L.HR_E8M0}
-_SCALE_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e8m0": torch.uint8}
+_SCALE_CODES = {"f32": L.HR_F32, "bf16": L.HR_BF16, "e8m0": L.HR_E8M0, "e4m3": L.HR_E4M3}
+_SCALE_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e8m0": torch.uint8, "e4m3": torch.uint8}
 
 
 @dataclass(frozen=True)
 class QSpec:
     """Quantizer spec: the pages' (wbits, groupsize, sym) plus format and
-    scale storage dtype ("f32" | "bf16" for INT, "e8m0" for MXFP4)."""
+    scale storage dtype ("f32" | "bf16" for INT, "e8m0" for MXFP4, "e4m3"
+    for NVFP4, whose tensor_scale g multiplies every block scale)."""
     format: str = "int"
     bits: int = 4
     group_size: int = 128
     sym: bool = True
     scale_dtype: str = "bf16"
+    tensor_scale: float = 1.0
 
     @staticmethod
     def mxfp4() -> "QSpec":
         return QSpec("mxfp4", 4, 32, True, "e8m0")
 
     @staticmethod
+    def nvfp4(tensor_scale: float = 1.0) -> "QSpec":
+        return QSpec("nvfp4", 4, 16, True, "e4m3", tensor_scale)
+
+    @staticmethod
     def from_dict(d: dict) -> "QSpec":
-        return QSpec(d["format"], int(d["bits"]), int(d["group_size"]), bool(d["sym"]), d["scale_dtype"])
+        return QSpec(d["format"], int(d["bits"]), int(d["group_size"]), bool(d["sym"]), d["scale_dtype"],
+                     float(d.get("tensor_scale", 1.0)))
 
     def c(self) -> L.hr_qspec:
-        fmt = {"int": L.HR_Q_INT, "mxfp4": L.HR_Q_MXFP4}[self.format]
+        fmt = {"int": L.HR_Q_INT, "mxfp4": L.HR_Q_MXFP4, "nvfp4": L.HR_Q_NVFP4}[self.format]
         return L.hr_qspec(fmt, self.bits, self.group_size, 1 if self.sym else 0,
-                          _SCALE_CODES[self.scale_dtype])
+                          _SCALE_CODES[self.scale_dtype], self.tensor_scale)
 
 
 def _dt(t: torch.Tensor) -> int:

@@ -12,8 +12,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libhadarot.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_EDEVICE = 0, -1, -2, -3
-HR_F32, HR_BF16, HR_E8M0 = 0, 1, 2
-HR_Q_INT, HR_Q_MXFP4 = 0, 1
+HR_F32, HR_BF16, HR_E8M0, HR_E4M3 = 0, 1, 2, 3
+HR_Q_INT, HR_Q_MXFP4, HR_Q_NVFP4 = 0, 1, 2
 
 # every exported symbol declared in include/hadarot.h
 EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
@@ -25,7 +25,7 @@ EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
 class hr_qspec(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
-                ("scale_dtype", ctypes.c_int32)]
+                ("scale_dtype", ctypes.c_int32), ("tensor_scale", ctypes.c_float)]
 
 
 class hr_qout(ctypes.Structure):

@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -64,17 +65,28 @@ bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi
 struct QSpec {
     int format, sym, logg, scale_dtype;
     int64_t g;
+    float tscale;  // NVFP4 tensor scale (1 otherwise)
 };
 
 int check_qspec(const hr_qspec* q, int64_t n, QSpec* out) {
     if (!q) return fail(HR_EINVAL, "quantizer spec is NULL");
-    if (q->format != HR_Q_INT && q->format != HR_Q_MXFP4)
-        return fail(HR_EINVAL, "quantizer format %d is not HR_Q_INT or HR_Q_MXFP4", q->format);
+    if (q->format != HR_Q_INT && q->format != HR_Q_MXFP4 && q->format != HR_Q_NVFP4)
+        return fail(HR_EINVAL, "quantizer format %d is not HR_Q_INT, HR_Q_MXFP4 or HR_Q_NVFP4", q->format);
     if (q->bits != 4) return fail(HR_EUNSUPPORTED, "bits = %d: only 4-bit codes are implemented", q->bits);
     const int64_t g = q->group_size;
+    float tscale = 1.0f;
     if (q->format == HR_Q_MXFP4) {
         if (g != 32) return fail(HR_EINVAL, "MXFP4 requires group_size 32 (got %lld)", (long long)g);
         if (q->scale_dtype != HR_E8M0) return fail(HR_EINVAL, "MXFP4 requires scale_dtype HR_E8M0");
+    } else if (q->format == HR_Q_NVFP4) {
+        if (g != 16) return fail(HR_EINVAL, "NVFP4 requires group_size 16 (got %lld)", (long long)g);
+        if (q->scale_dtype != HR_E4M3) return fail(HR_EINVAL, "NVFP4 requires scale_dtype HR_E4M3");
+        const float t = q->tensor_scale;
+        if (!(t >= 0.0f) || !std::isfinite(t))
+            return fail(HR_EINVAL, "NVFP4 tensor_scale must be positive and finite (0 means 1)");
+        // denormal tensor scales would flush to zero in the kernels
+        if (t != 0.0f && t < 1.17549435e-38f) return fail(HR_EINVAL, "NVFP4 tensor_scale is below the float range");
+        tscale = t == 0.0f ? 1.0f : t;
     } else {
         if (g <= 0 || g % 2) return fail(HR_EINVAL, "group_size %lld must be positive and even", (long long)g);
         if (q->sym != 0 && q->sym != 1) return fail(HR_EINVAL, "sym must be 0 or 1");
@@ -87,7 +99,8 @@ int check_qspec(const hr_qspec* q, int64_t n, QSpec* out) {
     out->sym = q->format == HR_Q_INT ? q->sym : 1;
     out->g = g;
     out->logg = ilog2(g);
-    out->scale_dtype = q->format == HR_Q_MXFP4 ? 2 : (q->scale_dtype == HR_BF16 ? 1 : 0);
+    out->scale_dtype = q->format == HR_Q_MXFP4 ? 2 : (q->format == HR_Q_NVFP4 ? 3 : (q->scale_dtype == HR_BF16 ? 1 : 0));
+    out->tscale = tscale;
     return HR_OK;
 }
 
@@ -217,6 +230,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
         a.q[i].sym = qs[i].sym;
         a.q[i].logg = qs[i].logg;
         a.q[i].scale_dtype = qs[i].scale_dtype;
+        a.q[i].tscale = qs[i].tscale;
     }
     if (geo.kron_k) {
         std::vector<int8_t> h;
@@ -231,7 +245,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     return HR_OK;
 }
 
-// Specialised bf16 kernels (one wave per 128 blocks of 32, per eight rows of
+// Specialised bf16 kernels (one wave per 128 blocks of 32 or 256 of 16, per eight rows of
 // 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
 // Kronecker row of K x 512) take the call when one is compiled for its exact
 // shape (randomised rotations: kwave); the generic kernel runs
@@ -246,7 +260,7 @@ int run(const hr::RotPlan& p, void* stream) {
     const bool signs_aligned =
         ((reinterpret_cast<uintptr_t>(a.in_signs) | reinterpret_cast<uintptr_t>(a.out_signs)) & 15) == 0;
     if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned &&
-        (a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
+        (a.logb == 4 || a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
         hr::FastArgs f{};
@@ -329,7 +343,7 @@ int check_qbuffers(const QSpec& q, int64_t rows, int64_t n, void* codes, void* s
         if (st) return st;
         b->zeros = {"zeros", reinterpret_cast<uintptr_t>(zeros), reinterpret_cast<uintptr_t>(zeros) + (size_t)((groups + 1) / 2)};
     } else if (zeros) {
-        return fail(HR_EINVAL, "%szeros must be NULL for a symmetric or MXFP4 quantizer", tag);
+        return fail(HR_EINVAL, "%szeros must be NULL for a symmetric, MXFP4 or NVFP4 quantizer", tag);
     }
     return HR_OK;
 }
@@ -644,6 +658,7 @@ int dequant_check(const void* codes, const void* scales, const void* zeros, cons
     a.sym = qs.sym;
     a.logg = qs.logg;
     a.scale_dtype = qs.scale_dtype;
+    a.tscale = qs.tscale;
     a.ref_bf16 = ref_dtype == HR_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hr::DqAccum* acc = nullptr;

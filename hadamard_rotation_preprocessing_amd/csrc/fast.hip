@@ -18,7 +18,8 @@
 //   blocks), no workgroup barrier.
 // k128: eight rows of 128 elements per wave; no LDS at all.
 // kkron<K>: one workgroup per row of K x 512 (Kronecker form).
-// kb32: 128 blocks of 32 per wave (rotation_size 32, MXFP4).
+// kb32 / kb16 (kbsmall): 128 blocks of 32 or 256 of 16 per wave
+//   (rotation_size 32 with MXFP4, 16 with NVFP4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -999,37 +1000,44 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
     }
 }
 
-// ----------------------------------------------------------------- kb32
-// Blocks of 32 (rotation_size 32, the MX block), MXFP4 codes or rotated
-// bf16. v_mfma_f32_16x16x32_bf16 with B = the data: column j is block j of a
-// run of 16 blocks (512 elements) and lane (j, g = lane / 16) holds its
-// elements 8 g .. 8 g + 7, one 16-byte load (so each load instruction reads
-// 1 KiB of consecutive bytes). Two MFMAs (A = the two row halves of H_32,
-// rows permuted) give lane (j, g) the outputs 8 g .. 8 g + 7 of block j:
-// D row 4 g + r of half h is output 8 g + 4 h + r. The whole transform is
-// exact bf16 x +-1 products summed in float32; no butterfly runs on the
-// vector ALU. An MX block's 32 values sit in lanes j, j + 16, j + 32, j + 48.
+// ----------------------------------------------------------- kb32 / kb16
+// Blocks of 32 (rotation_size 32, the MX block; MXFP4 codes or rotated bf16)
+// and of 16 (the NVFP block; NVFP4 codes or rotated bf16).
+// v_mfma_f32_16x16x32_bf16 with B = the data: column j is 32 consecutive
+// elements of a run of 512 (one block of 32, or two of 16) and lane
+// (j, g = lane / 16) holds its elements 8 g .. 8 g + 7, one 16-byte load (so
+// each load instruction reads 1 KiB of consecutive bytes). Two MFMAs (A = the
+// two row halves of H_32, or of blockdiag(H_16, H_16), rows permuted) give
+// lane (j, g) the outputs 8 g .. 8 g + 7 of column j: D row 4 g + r of half h
+// is output 8 g + 4 h + r. The whole transform is exact bf16 x +-1 products
+// summed in float32; no butterfly runs on the vector ALU. A block of 32 sits
+// in lanes j, j + 16, j + 32, j + 48; a block of 16 in lanes l, l ^ 16.
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-struct H32Table {
+template <int LOGB>
+struct HSmallTable {
     uint32_t w[2][64][4];   // [row half][lane][dword]
-    constexpr H32Table() : w() {
+    constexpr HSmallTable() : w() {
         for (int h = 0; h < 2; ++h)
             for (int l = 0; l < 64; ++l)
                 for (int t = 0; t < 8; ++t) {
                     const int i = l & 15, g = l >> 4;
                     const int out = 8 * (i >> 2) + 4 * h + (i & 3);   // output position of row i
                     const int in = 8 * g + t;                         // input position of k = 8 g + t
-                    int p = out & in, par = 0;
-                    while (p) {
-                        par ^= p & 1;
-                        p >>= 1;
+                    uint32_t v = 0;                                   // 0 across two blocks of 16
+                    if ((out >> LOGB) == (in >> LOGB)) {
+                        int p = out & in & ((1 << LOGB) - 1), par = 0;
+                        while (p) {
+                            par ^= p & 1;
+                            p >>= 1;
+                        }
+                        v = par ? 0xBF80u : 0x3F80u;
                     }
-                    const uint32_t v = par ? 0xBF80u : 0x3F80u;
                     w[h][l][t >> 1] |= v << (16 * (t & 1));
                 }
     }
 };
-__constant__ constexpr H32Table kH32 = H32Table();
+__constant__ constexpr HSmallTable<5> kH32 = HSmallTable<5>();
+__constant__ constexpr HSmallTable<4> kH16x2 = HSmallTable<4>();   // blockdiag(H_16, H_16)
 
 // maximum over lanes l, l ^ 16, l ^ 32, l ^ 48
 __device__ __forceinline__ float max_quad16(float v) {
@@ -1037,17 +1045,35 @@ __device__ __forceinline__ float max_quad16(float v) {
     return max_halves(v);
 }
 
-template <bool WROT, class Q0>
-__global__ void __launch_bounds__(256) kb32(const FastArgs a) {
-    static_assert(Q0::fmt == 1 || Q0::fmt < 0, "MXFP4 or rotation only");
+// E4M3 (OCP e4m3fn) byte of d >= 0: nearest, ties to the even mantissa,
+// saturating at 448.  From 2^-6 up, rounding the float32 pattern at mantissa
+// bit 20 leaves (biased exponent << 3 | three mantissa bits), and the byte is
+// that less (127 - 7) << 3; below 2^-6 the byte counts units of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_byte_f(float d) {
+    d = fminf(d, 448.0f);
+    const uint32_t u = __float_as_uint(d);
+    if (u >= 0x3C800000u) return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+    return static_cast<uint32_t>(rintf(d * 512.0f));
+}
+
+__device__ __forceinline__ float e4m3_value_f(uint32_t b) {
+    return (b >> 3) ? __uint_as_float((b + 960u) << 20) : static_cast<float>(b) * 0.001953125f;
+}
+
+template <int LOGB, bool WROT, class Q0>
+__global__ void __launch_bounds__(256) kbsmall(const FastArgs a) {
+    static_assert(LOGB == 4 || LOGB == 5, "blocks of 16 or 32");
+    static_assert(Q0::fmt < 0 || (LOGB == 5 && Q0::fmt == 1) || (LOGB == 4 && Q0::fmt == 2),
+                  "MXFP4 on blocks of 32, NVFP4 on blocks of 16, or rotation only");
     constexpr int CH = 8;                       // runs of 512 elements per wave
     const int lane = threadIdx.x & 63;
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t runs = a.units >> 4;          // units: blocks of 32 (a multiple of 16)
+    const int64_t runs = a.units >> (9 - LOGB);  // units: blocks (a whole number of runs)
     const int64_t run0 = wave * CH;
     if (run0 >= runs) return;
     const int j = lane & 15, g = lane >> 4;
-    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);
+    const uint32_t* tw = LOGB == 5 ? &kH32.w[0][lane][0] : &kH16x2.w[0][lane][0];
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(tw);   // hp[64]: the second row half
     const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
     const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
     const uint16_t* src = static_cast<const uint16_t*>(a.x);
@@ -1100,6 +1126,27 @@ __global__ void __launch_bounds__(256) kb32(const FastArgs a) {
                 if (g == 0) static_cast<uint8_t*>(a.q[0].scales)[e0 >> 5] = static_cast<uint8_t>(e + 127);
             }
         }
+        if constexpr (Q0::fmt == 2) {
+            // NVFP4: E4M3 byte of amax / (6 g); codes of y / s, s = E4M3 g, by
+            // the converter at scale 1 (a zero byte stores zero codes)
+            float am = fabsf(y[0]);
+#pragma unroll
+            for (int r = 1; r < 8; ++r) am = fmaxf(am, fabsf(y[r]));
+            am = fmaxf(am, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(am), 0x401F)));   // xor 16
+            const float ts = a.q[0].tscale;
+            const uint32_t byte = e4m3_byte_f(am / (6.0f * ts));
+            const float sc = e4m3_value_f(byte) * ts;
+            const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
+            float t[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] = y[r] * inv;
+            uint32_t wc = cvt8_fp4(t, 1.0f, 1.0f, false);
+            if (!(sc > 0.0f)) wc = 0u;
+            if (store) {
+                *reinterpret_cast<uint32_t*>(a.q[0].codes + (e0 >> 1)) = wc;
+                if ((g & 1) == 0) static_cast<uint8_t*>(a.q[0].scales)[e0 >> 4] = static_cast<uint8_t>(byte);
+            }
+        }
     }
 }
 
@@ -1109,7 +1156,7 @@ template <class Q>
 bool qmatch(const FastKey& k, int i) {
     if (Q::fmt < 0) return i >= k.nq;
     return i < k.nq && k.fmt[i] == Q::fmt && k.logg[i] == Q::logg && k.sdt[i] == Q::sdt &&
-           (Q::fmt == 1 || k.sym[i] == Q::sym);
+           (Q::fmt >= 1 || k.sym[i] == Q::sym);
 }
 
 template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
@@ -1142,12 +1189,15 @@ int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
 
-template <bool WROT, class Q0>
-int try_kb32(const FastKey& k, const FastArgs& a, hipStream_t s) {
-    if (k.mixed || k.logb != 5 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1 || (a.units & 15) != 0) return 0;
-    const int64_t waves = ((a.units >> 4) + 7) / 8;
+template <int LOGB, bool WROT, class Q0>
+int try_kbsmall(const FastKey& k, const FastArgs& a, hipStream_t s) {
+    constexpr int64_t per_run = 512 >> LOGB;    // blocks per run of 512 elements
+    if (k.mixed || k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1 ||
+        (a.units & (per_run - 1)) != 0)
+        return 0;
+    const int64_t waves = (a.units / per_run + 7) / 8;
     const int64_t grid = (waves + 3) / 4;
-    hipLaunchKernelGGL((kb32<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kbsmall<LOGB, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
@@ -1179,6 +1229,7 @@ using IA128B = QD<0, 0, 7, 1>;   // INT asym g128 bf16 scales
 using IS128F = QD<0, 1, 7, 0>;
 using IA128F = QD<0, 0, 7, 0>;
 using MX = QD<1, 1, 5, 2>;       // MXFP4
+using NV = QD<2, 1, 4, 3>;       // NVFP4
 
 }  // namespace
 int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
@@ -1245,9 +1296,12 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_k128<false, IS128B>(k, a, s)));
     HR_TRY((try_k128<true, IS128B>(k, a, s)));
     // blocks of 32
-    HR_TRY((try_kb32<false, MX>(k, a, s)));
-    HR_TRY((try_kb32<true, MX>(k, a, s)));
-    HR_TRY((try_kb32<true, QNone>(k, a, s)));
+    HR_TRY((try_kbsmall<5, false, MX>(k, a, s)));
+    HR_TRY((try_kbsmall<5, true, MX>(k, a, s)));
+    HR_TRY((try_kbsmall<5, true, QNone>(k, a, s)));
+    HR_TRY((try_kbsmall<4, false, NV>(k, a, s)));
+    HR_TRY((try_kbsmall<4, true, NV>(k, a, s)));
+    HR_TRY((try_kbsmall<4, true, QNone>(k, a, s)));
 #undef HR_TRY
     return 0;
 }

@@ -22,7 +22,7 @@
 //     Conformance) read element by element; with a permutation the loads
 //     are gathers within the row.
 //   * One normalisation multiply, optional store of the rotated tensor, and
-//     up to two fused quantizer epilogues (INT sym/asym groups, MXFP4) that
+//     up to two fused quantizer epilogues (INT sym/asym groups, MXFP4, NVFP4) that
 //     reduce group statistics across the threads of a group with lane
 //     shuffles (and LDS across waves), round, pack nibbles and store.
 #include <hip/hip_runtime.h>
@@ -246,6 +246,21 @@ __device__ __forceinline__ void kron_mix(float (&v)[1 << LOGE], float* lds, int 
 
 // ---------------------------------------------------------------- epilogue
 
+// E4M3 (OCP e4m3fn) byte of d >= 0: nearest, ties to the even mantissa,
+// saturating at 448.  From 2^-6 up, rounding the float32 pattern at mantissa
+// bit 20 leaves (biased exponent << 3 | three mantissa bits), and the byte is
+// that less (127 - 7) << 3; below 2^-6 the byte counts units of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_byte(float d) {
+    d = fminf(d, 448.0f);
+    const uint32_t u = __float_as_uint(d);
+    if (u >= 0x3C800000u) return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+    return static_cast<uint32_t>(rintf(d * 512.0f));
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+    return (b >> 3) ? __uint_as_float((b + 960u) << 20) : static_cast<float>(b) * 0.001953125f;
+}
+
 template <int LOGE>
 __device__ __forceinline__ void quantize(const float (&y)[1 << LOGE], const QuantDev& q, int64_t total_groups,
                                          int tid, int nt, bool valid, int64_t e0, int64_t wg_e0,
@@ -308,6 +323,24 @@ __device__ __forceinline__ void quantize(const float (&y)[1 << LOGE], const Quan
             w[j >> 3] |= idx << (4 * (j & 7));
         }
         if (leader) static_cast<uint8_t*>(q.scales)[G] = static_cast<uint8_t>(e + 127);
+    } else if (q.format == 2) {
+        // NVFP4: E4M3 block scale of amax / (6 g); E2M1 elements of y / s with
+        // s = E4M3 g; a zero scale leaves every code 0
+        const float amax = fmaxf(r0, r1);
+        const uint32_t byte = e4m3_byte(amax / (6.0f * q.tscale));
+        const float s = e4m3_value(byte) * q.tscale;
+        if (s > 0.0f) {
+            const float inv = 1.0f / s;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const float a = fabsf(y[j] * inv);
+                uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                               (a >= 3.5f) + (a > 5.0f);
+                idx |= (y[j] < 0.0f) ? 8u : 0u;
+                w[j >> 3] |= idx << (4 * (j & 7));
+            }
+        }
+        if (leader) static_cast<uint8_t*>(q.scales)[G] = static_cast<uint8_t>(byte);
     } else {
         float s;
         float zf = 0.0f;
@@ -457,6 +490,11 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
                 const float m = e2m1_mag(c);
                 deq = ldexpf((c & 8u) ? -m : m, ee);
                 step = 0.0f;  // set below from the reference
+            } else if (a.format == 2) {
+                s = e4m3_value(static_cast<const uint8_t*>(a.scales)[G]) * a.tscale;
+                const float m = e2m1_mag(c);
+                deq = ((c & 8u) ? -m : m) * s;
+                step = 0.0f;  // set below from the reference
             } else {
                 s = (a.scale_dtype == 1) ? bf2f(static_cast<const uint16_t*>(a.scales)[G])
                                          : static_cast<const float*>(a.scales)[G];
@@ -483,6 +521,13 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
                     const float v = fabsf(ldexpf(r, -ee));
                     const float sp = (v < 2.0f) ? 0.5f : ((v < 4.0f) ? 1.0f : 2.0f);
                     step = ldexpf(sp, ee);
+                    clamped = v > 6.0f;
+                } else if (a.format == 2) {
+                    // a zero block scale is measured against the smallest one, 2^-9 g
+                    const float sb = s > 0.0f ? s : 0.001953125f * a.tscale;
+                    const float v = fabsf(r) / sb;
+                    const float sp = (v < 2.0f) ? 0.5f : ((v < 4.0f) ? 1.0f : 2.0f);
+                    step = sp * sb;
                     clamped = v > 6.0f;
                 } else {
                     const float t = r / s + z;

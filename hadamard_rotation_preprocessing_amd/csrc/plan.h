@@ -15,10 +15,11 @@ constexpr int kMaxKron = 64;   // largest Kronecker base order handled on the GP
 
 // One quantizer epilogue, resolved to device pointers.
 struct QuantDev {
-    int32_t format;       // 0 INT, 1 MXFP4
+    int32_t format;       // 0 INT, 1 MXFP4, 2 NVFP4
     int32_t sym;          // INT: 1 symmetric, 0 asymmetric
     int32_t logg;         // log2(group_size)
-    int32_t scale_dtype;  // 0 f32, 1 bf16, 2 e8m0
+    int32_t scale_dtype;  // 0 f32, 1 bf16, 2 e8m0, 3 e4m3
+    float tscale;         // NVFP4 tensor scale g (1 otherwise)
     uint8_t* codes;
     void* scales;
     uint8_t* zeros;       // INT asymmetric only
@@ -70,6 +71,7 @@ struct DqArgs {
     void* stats;           // nullable: DqAccum on the device
     int64_t total;         // elements
     int32_t format, sym, logg, scale_dtype, ref_bf16;
+    float tscale;          // NVFP4 tensor scale
 };
 
 // Device accumulators of dequant_check.

@@ -18,8 +18,8 @@
  *     the offline weight side (section 1.1, online vs offline).
  *   - Group round-to-nearest quantization with the (wbits, groupsize, sym)
  *     specification (OneCompression "Pre-Process", Workflow note; orbitquant
- *     0.2.0, Method Conformance: INT4 group RTN) and MXFP4 with blocks of 32
- *     (AutoRound page, sections 2 and 2.1).
+ *     0.2.0, Method Conformance: INT4 group RTN), MXFP4 with blocks of 32
+ *     and NVFP4 with blocks of 16 (AutoRound page, sections 2 and 2.1).
  *
  * Conventions shared by every call
  *   - Tensors are contiguous row-major; the rotated dimension n is the last
@@ -45,7 +45,8 @@
  *     magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; sign set iff y < 0.
  *   - Packing: 4-bit codes two per byte, element 2j in the low nibble
  *     (symmetric codes as two's complement nibbles), `rows * n / 2` bytes.
- *     Scales: rows * n / group_size values of the scale dtype (E8M0: bytes).
+ *     Scales: rows * n / group_size values of the scale dtype (E8M0 and
+ *     E4M3: bytes).
  *     Zero points (asymmetric only): uint4, two per byte over the row-major
  *     flattened group index, ceil(groups / 2) bytes, a trailing odd nibble
  *     set to 0.
@@ -85,24 +86,34 @@ typedef enum hr_status {
 typedef enum hr_dtype {
     HR_F32 = 0,
     HR_BF16 = 1,
-    HR_E8M0 = 2            /* scales only: MXFP4 shared exponent byte */
+    HR_E8M0 = 2,           /* scales only: MXFP4 shared exponent byte */
+    HR_E4M3 = 3            /* scales only: NVFP4 block scale byte (OCP e4m3fn) */
 } hr_dtype;
 
 typedef enum hr_qformat {
     HR_Q_INT = 0,          /* round-to-nearest integer groups */
-    HR_Q_MXFP4 = 1         /* E2M1 elements, E8M0 scale per 32 */
+    HR_Q_MXFP4 = 1,        /* E2M1 elements, E8M0 scale per 32 */
+    HR_Q_NVFP4 = 2         /* E2M1 elements, E4M3 scale per 16, times a tensor scale */
 } hr_qformat;
 
 /* Quantizer specification: the pages' (wbits, groupsize, sym) plus format
  * and scale storage type.  INT: bits must be 4, group_size an even power of
  * two dividing n, scale_dtype HR_F32 or HR_BF16.  MXFP4: bits 4,
- * group_size 32, sym ignored, scale_dtype HR_E8M0. */
+ * group_size 32, sym ignored, scale_dtype HR_E8M0.
+ * NVFP4 (named on the AutoRound page, sections 2 and 2.1, with rotation
+ * blocks of 16; the encoding is the public two-level one): bits 4,
+ * group_size 16, sym ignored, scale_dtype HR_E4M3; tensor_scale g > 0 and
+ * finite (0 means 1).  Block byte = E4M3 of amax / (6 g), nearest even,
+ * saturating at 448; element codes = E2M1 of y / (E4M3 g), nearest even,
+ * saturating at 6 (all 0 when the byte is 0).  tensor_scale is ignored by
+ * the other formats. */
 typedef struct hr_qspec {
     int32_t format;        /* hr_qformat */
     int32_t bits;
     int32_t group_size;
     int32_t sym;           /* 1 symmetric, 0 asymmetric (INT only) */
     int32_t scale_dtype;   /* hr_dtype */
+    float tensor_scale;    /* NVFP4 only */
 } hr_qspec;
 
 /* Output buffers of one quantizer. zeros is NULL unless INT asymmetric. */
@@ -189,7 +200,8 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
 /*
  * Dequantize packed codes (orbitquant 0.2.0, "Packed Runtime": an explicit
  * dequantized reference mode for numerical debugging):
- *   INT symmetric q * s; INT asymmetric (q - z) * s; MXFP4 E2M1 * 2^e.
+ *   INT symmetric q * s; INT asymmetric (q - z) * s; MXFP4 E2M1 * 2^e;
+ *   NVFP4 E2M1 * E4M3 * tensor_scale.
  *   codes, scales, zeros  as written by the calls above for [rows, n].
  *   ref    device or NULL: [rows, n] of ref_dtype (HR_F32 / HR_BF16).
  *   deq    device or NULL: [rows, n] float32 output.

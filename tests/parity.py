@@ -4,7 +4,7 @@ Rotated values: per element |gpu - oracle| <= tol * ||oracle row||_2, with
 tol = 2e-3 for bfloat16 outputs and 1e-5 for float32 (the oracle value is the
 unrounded float64 rotation).
 
-Integer codes (INT and MXFP4) must be bit-exact except where the oracle's
+Integer codes (INT, MXFP4 and NVFP4) must be bit-exact except where the oracle's
 pre-rounding value lies within 1e-3 of a step from a rounding boundary, and
 then the codes may differ by one step only (adjacent code).  Scales: float32
 within 1e-6 relative; bfloat16 and E8M0 exact, except a group whose unrounded
@@ -14,7 +14,10 @@ hold the neighbouring value; such a group's codes are re-derived by the
 oracle from the GPU's stored scale before the code rule is applied.  Zero
 points follow the code rule with pre-rounding value -lo / s.  A code 0x0 /
 0x8 (MXFP4 +0 / -0) difference is accepted where |y / 2^e| < 5e-4 (the sign of
-a value at the float32 rounding-noise level).
+a value at the float32 rounding-noise level).  NVFP4 E4M3 block bytes follow
+the bfloat16 scale rule (the rounding point is the midpoint between adjacent
+E4M3 values), and its codes the MXFP4 code rule with y / s in place of
+y / 2^e.
 
 Two bounds derived from the arithmetic extend the stated tolerances where
 those cannot hold for any correct implementation:
@@ -227,5 +230,56 @@ def check_mxfp4(gpu: dict, y: np.ndarray, rep: Report, kron_k: int = 0):
         if bad.any():
             i = np.argwhere(bad)[0]
             raise AssertionError("MXFP4 code mismatch at %s: gpu %d oracle %d (pre %r)"
+                                 % (tuple(i), codes[tuple(i)], exp[tuple(i)], pre[tuple(i)]))
+        rep.code_mismatch += int(d.sum())
+
+
+def check_nvfp4(gpu: dict, y: np.ndarray, rep: Report, tensor_scale: float = 1.0, kron_k: int = 0):
+    """NVFP4 under the MXFP4 rules: E4M3 block bytes exact except an adjacent
+    byte where amax / (6 g) lies within 1e-6 relative of the midpoint between
+    the two values (that block's codes are then re-derived from the GPU's
+    byte); codes exact except adjacent codes near a rounding boundary, and
+    +0 / -0 at the rounding-noise level."""
+    rows, n = y.shape
+    g = 16
+    ts = float(np.float32(tensor_scale)) if tensor_scale else 1.0
+    ref = oracle.nvfp4_quant(y, g, ts)
+    codes = unpack_gpu_codes(gpu["codes"], rows * n, False).reshape(rows, n)
+    b_gpu = gpu["scales"].cpu().numpy().astype(np.int64).reshape(rows, n // g)
+    b_ref = ref.scales
+    rep.n_elems += rows * n
+    rep.n_groups += rows * n // g
+    ey = eps_row(y, kron_k)
+    flip = b_gpu != b_ref
+    if flip.any():
+        mid = 0.5 * (oracle.e4m3_decode(np.clip(b_gpu, 0, 126)) + oracle.e4m3_decode(b_ref))
+        near = np.abs(ref.raw - mid) <= np.maximum(SCALE_REL * ref.raw, ey / (6.0 * ts))
+        bad = flip & ~(near & (np.abs(b_gpu - b_ref) == 1))
+        if bad.any():
+            i = np.argwhere(bad)[0]
+            raise AssertionError("E4M3 mismatch at group %s: gpu %d oracle %d (amax / 6g %r)"
+                                 % (tuple(i), b_gpu[tuple(i)], b_ref[tuple(i)], ref.raw[tuple(i)]))
+        rep.scale_flips += int(flip.sum())
+    s_use = oracle.e4m3_decode(np.where(flip, b_gpu, b_ref)) * ts
+    yg = y.reshape(rows, n // g, g)
+    safe = np.where(s_use > 0, s_use, 1.0)
+    pre = np.where(s_use[..., None] > 0, yg / safe[..., None], 0.0).reshape(rows, n)
+    exp = np.where(np.repeat(s_use, g, axis=1) > 0, oracle.e2m1_round(pre), 0)
+    d = codes != exp
+    if d.any():
+        a = np.abs(pre)
+        k = np.clip(np.searchsorted(_BOUNDS, a), 0, len(_BOUNDS) - 1)
+        dist = np.minimum(
+            np.abs(a - _BOUNDS[np.clip(k - 1, 0, 6)]) / _SPACING[np.clip(k - 1, 0, 6)],
+            np.abs(a - _BOUNDS[k]) / _SPACING[k])
+        same_sign = (codes & 8) == (exp & 8)
+        adjacent = same_sign & (np.abs((codes & 7) - (exp & 7)) == 1)
+        etol = np.repeat(np.maximum(CODE_TOL, ey / safe / 0.5), g, axis=1)
+        zero_sign = ((codes & 7) == 0) & ((exp & 7) == 0) & (a < 0.5 * etol)
+        ok = ((dist <= etol) & adjacent) | zero_sign
+        bad = d & ~ok
+        if bad.any():
+            i = np.argwhere(bad)[0]
+            raise AssertionError("NVFP4 code mismatch at %s: gpu %d oracle %d (pre %r)"
                                  % (tuple(i), codes[tuple(i)], exp[tuple(i)], pre[tuple(i)]))
         rep.code_mismatch += int(d.sum())

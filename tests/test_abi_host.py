@@ -35,8 +35,8 @@ def test_exports_every_header_symbol():
         assert hasattr(lib, n), n
 
 
-def q(fmt=L.HR_Q_INT, bits=4, g=128, sym=1, sd=L.HR_BF16):
-    return ctypes.byref(L.hr_qspec(fmt, bits, g, sym, sd))
+def q(fmt=L.HR_Q_INT, bits=4, g=128, sym=1, sd=L.HR_BF16, ts=0.0):
+    return ctypes.byref(L.hr_qspec(fmt, bits, g, sym, sd, ts))
 
 
 def rqa(x=A, dt=L.HR_BF16, rows=16, n=4096, block=0, qs=None, codes=B, scales=C, zeros=NUL, yrot=NUL):
@@ -63,6 +63,14 @@ def msg():
     (dict(qs=q(sd=L.HR_E8M0)), L.HR_EINVAL, "INT scales"),
     (dict(qs=q(fmt=L.HR_Q_MXFP4, g=64, sd=L.HR_E8M0)), L.HR_EINVAL, "32"),
     (dict(qs=q(fmt=L.HR_Q_MXFP4, g=32, sd=L.HR_BF16)), L.HR_EINVAL, "E8M0"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=32, sd=L.HR_E4M3)), L.HR_EINVAL, "16"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E8M0)), L.HR_EINVAL, "E4M3"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E4M3, ts=-1.0)), L.HR_EINVAL, "tensor_scale"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E4M3, ts=float("inf"))), L.HR_EINVAL, "tensor_scale"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E4M3, ts=float("nan"))), L.HR_EINVAL, "tensor_scale"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E4M3, ts=1e-40)), L.HR_EINVAL, "float range"),
+    (dict(qs=q(fmt=L.HR_Q_NVFP4, g=16, sd=L.HR_E4M3), zeros=D), L.HR_EINVAL, "NULL"),
+    (dict(qs=q(sd=L.HR_E4M3)), L.HR_EINVAL, "INT scales"),
     (dict(qs=q(fmt=5)), L.HR_EINVAL, "format"),
     (dict(x=NUL), L.HR_EINVAL, "x is NULL"),
     (dict(x=ctypes.c_void_p(P + 8)), L.HR_EINVAL, "aligned"),

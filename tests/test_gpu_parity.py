@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import hadamard_rotation_preprocessing_amd as hr
-from parity import Report, check_int, check_mxfp4, check_rotated, to_np64
+from parity import Report, check_int, check_mxfp4, check_nvfp4, check_rotated, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,8 @@ def run_act(x, n, block, spec, y_rot=False, ref_y=None):
         check_rotated(to_np64(out["y_rot"]).reshape(-1, n), y, dtname(x), rep)
     if spec.format == "mxfp4":
         check_mxfp4(out, y, rep, kron_k=kk)
+    elif spec.format == "nvfp4":
+        check_nvfp4(out, y, rep, spec.tensor_scale, kron_k=kk)
     else:
         check_int(out, y, spec.group_size, spec.sym, spec.scale_dtype, rep, kron_k=kk)
     say("  ", rep)
@@ -318,6 +320,8 @@ def test_mixed_rotate_quantize(case):
     check_rotated(to_np64(out["y_rot"]).reshape(-1, n), y, dtname(x), rep)
     if spec.format == "mxfp4":
         check_mxfp4(out, y, rep, kron_k=kk)
+    elif spec.format == "nvfp4":
+        check_nvfp4(out, y, rep, spec.tensor_scale, kron_k=kk)
     else:
         check_int(out, y, spec.group_size, spec.sym, spec.scale_dtype, rep, kron_k=kk)
     say("  ", rep)
@@ -370,6 +374,83 @@ def test_mixed_weight_fusion():
     check_rotated(to_np64(out["w_rot"]).reshape(-1, n), y, "bf16", rep)
     check_mxfp4(out["quant"][0], y, rep)
     check_int(out["quant"][1], y, 128, True, "bf16", rep)
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def _tensor_scale(x, n, block):
+    """The two-level choice g = amax(tensor) / (448 * 6), from the oracle's
+    rotation, rounded to float32 (what the C ABI carries)."""
+    return float(np.float32(np.abs(oracle.rotate(x, n, block)).max() / (448.0 * 6.0)))
+
+
+@pytest.mark.parametrize("shape", [(67, 4096, 16), (37, 14336, 16), (19, 4096, 0), (23, 2048, 128),
+                                   (5, 32, 16), (9, 14336, 0)],
+                         ids=["r1-b16", "r4-b16", "r1-full", "b128", "tiny", "r4-kron"])
+@pytest.mark.parametrize("scale", ["unit", "two-level"])
+def test_nvfp4_activations(kernel_path, shape, scale):
+    rows, n, block = shape
+    x = synth.gaussian((rows, n), seed=rows * 7 + n + block, dtype=torch.bfloat16)
+    x[1] *= 50.0                     # one outlier row
+    x[2, :] = 0.0
+    ts = 1.0 if scale == "unit" else _tensor_scale(x, n, block)
+    run_act(x, n, block, hr.QSpec.nvfp4(ts), y_rot=(scale == "unit"))
+
+
+@pytest.mark.parametrize("rows", [64, 3])
+def test_block16_rotate_and_weight(kernel_path, rows):
+    """Rotation only and W . R + NVFP4 with blocks of 16 (the specialised
+    path takes whole runs of 512 elements: 64 rows of 4096 do, 3 rows of 80
+    do not)."""
+    n = 4096 if rows == 64 else 80
+    x = synth.gaussian((rows, n), seed=41 + rows, dtype=torch.bfloat16)
+    say("hadamard_rotate block 16", rows, n)
+    y = hr.rotate(x.to(DEV), 16)
+    torch.cuda.synchronize()
+    ref = oracle.rotate(x, n, 16)
+    check_rotated(to_np64(y), ref, "bf16")
+    say("rotate_fuse_weight block 16 NVFP4", rows, n)
+    out = hr.rotate_fuse_weight(x.to(DEV), 16, [hr.QSpec.nvfp4(0.5)])
+    torch.cuda.synchronize()
+    rep = Report()
+    check_rotated(to_np64(out["w_rot"]), ref, "bf16", rep)
+    check_nvfp4(out["quant"][0], ref, rep, 0.5)
+
+
+def test_nvfp4_float32_and_extremes():
+    n = 1024
+    x = synth.gaussian((12, n), seed=31, dtype=torch.float32)
+    x[0] = 0.0                       # all-zero blocks: byte 0, codes 0
+    x[1] *= 1e-5                     # block scales in the E4M3 subnormal range or 0
+    x[2] *= 1e4                      # scales saturate at 448, codes at 6
+    x[3, :16] = torch.tensor([6.0, 3.0, 1.75, 0.25] * 4)   # ties on the E2M1 grid
+    for ts in (1.0, 0.03125, 3.0):
+        run_act(x, n, 16, hr.QSpec.nvfp4(ts), y_rot=True)
+
+
+def test_nvfp4_weight_fusion_and_dequant():
+    """W . R with NVFP4 and int4 from one read; dequant_check of the NVFP4
+    codes against the oracle's dequantization."""
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=96, in_features=4096)
+    specs = [hr.QSpec.nvfp4(0.01), hr.QSpec("int", 4, 128, True, "bf16")]
+    say("rotate_fuse_weight NVFP4 + INT", tuple(w.shape))
+    out = hr.rotate_fuse_weight(w.to(DEV), 16, specs)
+    torch.cuda.synchronize()
+    y = oracle.rotate(w, 4096, 16)
+    rep = Report()
+    check_rotated(to_np64(out["w_rot"]), y, "bf16", rep)
+    q = out["quant"][0]
+    check_nvfp4(q, y, rep, 0.01)
+    check_int(out["quant"][1], y, 128, True, "bf16", rep)
+    deq, st = hr.dequant_check(q, specs[0], 96, 4096, ref=out["w_rot"])
+    codes = oracle.unpack_nibbles(q["codes"].cpu().numpy(), 96 * 4096).reshape(96, 4096)
+    ref_deq = oracle.dequant_nvfp4(codes, q["scales"].cpu().numpy().astype(np.int64), 16,
+                                   float(np.float32(0.01)))
+    assert np.allclose(to_np64(deq), ref_deq, rtol=2e-7, atol=0)
+    # the E4M3 scale may round amax / 6 down by up to 1/16, so a block's
+    # largest element can sit past 6 (clamped); never more than one per block
+    assert st["n_clamped"] <= 96 * 4096 // 16 and 0 < st["rel_l2_err"] < 0.2
+    say("  ", rep, st)
 
 
 # ------------------------------------------- output-side weight fusion (R^T W)
