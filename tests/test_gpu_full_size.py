@@ -3,7 +3,7 @@ bench.py times: the whole tensor is rotated and quantized on the GPU, and a
 seeded sample of rows (the first, the last and random ones) is compared with
 the oracle row by row, with the same tolerances as the reduced-size tests.
 Every output is also checked for properties that hold at any size (scales
-positive, E8M0 bytes below 255, zero points in range)."""
+positive, E8M0 bytes below 255, E4M3 bytes at most 448, zero points in range)."""
 import sys
 
 import numpy as np
@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import hadamard_rotation_preprocessing_amd as hr
-from parity import Report, check_int, check_mxfp4, check_rotated, to_np64
+from parity import Report, check_int, check_mxfp4, check_nvfp4, check_rotated, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -51,6 +51,10 @@ def check_quant_rows(out, spec, y, idx, n, rep, kron_k=0):
         check_mxfp4(sub, y, rep, kron_k=kron_k)
         e = out["scales"].cpu().numpy()
         assert e.max() < 255
+    elif spec.format == "nvfp4":
+        check_nvfp4(sub, y, rep, spec.tensor_scale, kron_k=kron_k)
+        b = out["scales"].cpu().numpy()
+        assert b.max() <= 126                      # 448 at most, never the NaN byte
     else:
         zg = None
         if not spec.sym:
@@ -166,3 +170,31 @@ def test_randomised_full_size(name, block, pm, si, so):
     rep = Report()
     check_quant_rows(out, spec, y, idx, n, rep)
     say("  ", rep)
+
+
+@pytest.mark.parametrize("name", ["r1", "r4"])
+def test_block16_nvfp4_full_size(name):
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w)
+    spec = hr.QSpec.nvfp4()
+    rows, n = x.shape
+    say(name, "full size, block 16, NVFP4", rows, n)
+    out = hr.alloc_quant_outputs(rows, n, spec, DEV)
+    hr.rotate_quantize_act(x.to(DEV), 16, spec, out=out)
+    torch.cuda.synchronize()
+    idx = sample_rows(rows, 48, 6)
+    rep = Report()
+    check_quant_rows(out, spec, oracle.rotate(x[torch.as_tensor(idx)], n, 16), idx, n, rep)
+    say("  ", rep)
+
+
+def test_down_proj_output_fusion_full_size():
+    """rotate_fuse_weight_out on down_proj [4096, 14336] as bench.py times it,
+    checked on sampled columns (each a full-length transform)."""
+    w = synth.gaussian((4096, 14336), seed=104, dtype=torch.bfloat16)
+    say("down_proj output fusion full size")
+    wr = hr.rotate_fuse_weight_out(w.to(DEV), 0)
+    torch.cuda.synchronize()
+    cols = sample_rows(14336, 48, 7)
+    ref = oracle.rotate_out(w[:, torch.as_tensor(cols)], 4096, 0)
+    check_rotated(to_np64(wr[:, torch.as_tensor(cols, device=DEV)]).T.copy(), ref.T.copy(), "bf16")
