@@ -34,6 +34,7 @@ typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // fma(y, c, kMagic) = kMagic + rne(y * c) for |y * c| < 2^22: the rounded
 // integer sits in the low mantissa bits (one rounding of the exact product).
@@ -100,6 +101,38 @@ __device__ __forceinline__ f32x4_t mfma_h16(bf16x4_t h, uint32_t lo, uint32_t hi
     const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(h, b, z, 0, 0, 0);
 }
+
+// A operands of v_mfma_f32_16x16x32_bf16 for a transform of five index bits
+// of 32 values: lane (j, g = lane / 16) holds k = 8 g + t (t = 0..7) of B
+// column j, and the two row halves h give lane (j, g) the outputs
+// 8 g + 4 h + r (r = 0..3), i.e. the outputs land where their inputs were.
+// HSmallTable<5> is H_32 on (t, g); HSmallTable<4> is blockdiag(H_16, H_16).
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+template <int LOGB>
+struct HSmallTable {
+    uint32_t w[2][64][4];   // [row half][lane][dword]
+    constexpr HSmallTable() : w() {
+        for (int h = 0; h < 2; ++h)
+            for (int l = 0; l < 64; ++l)
+                for (int t = 0; t < 8; ++t) {
+                    const int i = l & 15, g = l >> 4;
+                    const int out = 8 * (i >> 2) + 4 * h + (i & 3);   // output position of row i
+                    const int in = 8 * g + t;                         // input position of k = 8 g + t
+                    uint32_t v = 0;                                   // 0 across two blocks of 16
+                    if ((out >> LOGB) == (in >> LOGB)) {
+                        int p = out & in & ((1 << LOGB) - 1), par = 0;
+                        while (p) {
+                            par ^= p & 1;
+                            p >>= 1;
+                        }
+                        v = par ? 0xBF80u : 0x3F80u;
+                    }
+                    w[h][l][t >> 1] |= v << (16 * (t & 1));
+                }
+    }
+};
+__constant__ constexpr HSmallTable<5> kH32 = HSmallTable<5>();
+__constant__ constexpr HSmallTable<4> kH16x2 = HSmallTable<4>();   // blockdiag(H_16, H_16)
 
 template <int N, unsigned MASK>
 __device__ __forceinline__ void bfly(float (&v)[N]) {
@@ -371,8 +404,9 @@ struct KW {
 };
 
 // Load layout L0: element e = 512 c + 8 lane + r of the wave's 4096 (chunk c,
-// r = 0..7).  The MFMA transforms index bits {0, 1, 7, 8}; register
-// butterflies bits 2, 9, 10 and (4096-blocks) 11; an LDS transpose in NS
+// r = 0..7).  The MFMA (16x16x32, one 16-byte load as B) transforms index
+// bits {0, 1, 2, 7, 8}; register butterflies bits 9, 10 and (4096-blocks)
+// 11; an LDS transpose in NS
 // passes over r gives each lane 64 contiguous elements (L2); bits 3..5 are
 // then register bits and bit 6 is lane bit 0 (DPP).  For 2048-blocks bit 11
 // selects the block and is never mixed.
@@ -492,21 +526,24 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         }
     }
 
-    const bf16x4_t hop = h16_operand(lane);
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);   // hp[64]: row half 1
+    const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
+    const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
     float v[E];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const f32x4_t d0 = mfma_h16(hop, raw[c][0], raw[c][1]);
-        const f32x4_t d1 = mfma_h16(hop, raw[c][2], raw[c][3]);
+        const bf16x8_t Bc = __builtin_bit_cast(bf16x8_t, raw[c]);
+        const f32x4v_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Bc, f32x4v_t{}, 0, 0, 0);
+        const f32x4v_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bc, f32x4v_t{}, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             v[8 * c + j] = d0[j];
             v[8 * c + 4 + j] = d1[j];
         }
     }
-    // register bits of L0: v-index bit 2 (e bit 2), bits 3..5 (e bits 9..11);
-    // e bit 11 only inside a 4096 block
-    bfly<E, (LOGB == 12) ? 0x3Cu : 0x1Cu>(v);
+    // register bits of L0: v-index bits 3..5 (e bits 9..11); e bit 11 only
+    // inside a 4096 block
+    bfly<E, (LOGB == 12) ? 0x38u : 0x18u>(v);
 
     // transpose L0 -> lane-contiguous, in NS passes over r
     float y[E];
@@ -716,7 +753,6 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
 
 // ----------------------------------------------------------------- kkron
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Hides a value from the optimiser, so that per-lane LDS bases stay whole
 // and the constant parts of addresses stay in the instruction offsets.
@@ -1012,33 +1048,6 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
 // is output 8 g + 4 h + r. The whole transform is exact bf16 x +-1 products
 // summed in float32; no butterfly runs on the vector ALU. A block of 32 sits
 // in lanes j, j + 16, j + 32, j + 48; a block of 16 in lanes l, l ^ 16.
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-template <int LOGB>
-struct HSmallTable {
-    uint32_t w[2][64][4];   // [row half][lane][dword]
-    constexpr HSmallTable() : w() {
-        for (int h = 0; h < 2; ++h)
-            for (int l = 0; l < 64; ++l)
-                for (int t = 0; t < 8; ++t) {
-                    const int i = l & 15, g = l >> 4;
-                    const int out = 8 * (i >> 2) + 4 * h + (i & 3);   // output position of row i
-                    const int in = 8 * g + t;                         // input position of k = 8 g + t
-                    uint32_t v = 0;                                   // 0 across two blocks of 16
-                    if ((out >> LOGB) == (in >> LOGB)) {
-                        int p = out & in & ((1 << LOGB) - 1), par = 0;
-                        while (p) {
-                            par ^= p & 1;
-                            p >>= 1;
-                        }
-                        v = par ? 0xBF80u : 0x3F80u;
-                    }
-                    w[h][l][t >> 1] |= v << (16 * (t & 1));
-                }
-    }
-};
-__constant__ constexpr HSmallTable<5> kH32 = HSmallTable<5>();
-__constant__ constexpr HSmallTable<4> kH16x2 = HSmallTable<4>();   // blockdiag(H_16, H_16)
-
 // maximum over lanes l, l ^ 16, l ^ 32, l ^ 48
 __device__ __forceinline__ float max_quad16(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));   // xor 16
