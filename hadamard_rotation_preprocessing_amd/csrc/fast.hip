@@ -6,7 +6,8 @@
 // product of 2x2 butterflies over the index bits, so the bits can be taken in
 // any order and by any mechanism:
 //   * bits of exact bf16 inputs by an MFMA: a lane's loaded bf16 values are
-//     B operand columns and A is a +-1 matrix (H_16, H_32, or H_K (x) H_4),
+//     B operand columns and A is a +-1 matrix (H_32, blockdiag(H_16, H_16),
+//     or H_K (x) H_4),
 //     so D = A . X transforms those bits exactly (bf16 products with +-1 are
 //     exact, accumulation is float32);
 //   * bits held in registers: butterflies a +- b;
@@ -30,8 +31,6 @@
 namespace hr {
 namespace {
 
-typedef short bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -67,40 +66,6 @@ __device__ __forceinline__ u32x4_t ldc16(const void* p) { return *static_cast<co
 // Ordinary stores: a lane's consecutive 16-byte pieces of one cache line are
 // merged in L2 (streaming stores of such partial lines are far slower).
 __device__ __forceinline__ void stg16(void* p, u32x4_t v) { *static_cast<u32x4_t*>(p) = v; }
-
-// A operand H_16: lane l holds H_16[l % 16][4 (l / 16) + t], t = 0..3, as
-// two dwords of packed bf16 (+1 = 0x3F80, -1 = 0xBF80), element t = 0 lowest.
-struct H16Table {
-    uint32_t w[128];
-    constexpr H16Table() : w() {
-        for (int l = 0; l < 64; ++l)
-            for (int t = 0; t < 4; ++t) {
-                const int i = l & 15, k = 4 * (l >> 4) + t;
-                int p = i & k, par = 0;
-                while (p) {
-                    par ^= p & 1;
-                    p >>= 1;
-                }
-                const uint32_t h = par ? 0xBF80u : 0x3F80u;
-                w[2 * l + (t >> 1)] |= h << (16 * (t & 1));
-            }
-    }
-};
-__constant__ constexpr H16Table kH16 = H16Table();
-
-__device__ __forceinline__ bf16x4_t h16_operand(int lane) {
-    const u32x2_t u = {kH16.w[2 * lane], kH16.w[2 * lane + 1]};
-    return __builtin_bit_cast(bf16x4_t, u);
-}
-
-// Transform of the four index bits (k & 3 within the lane, k >> 2 across
-// lanes l, l + 16, l + 32, l + 48) of the four bf16 values in (lo, hi).
-__device__ __forceinline__ f32x4_t mfma_h16(bf16x4_t h, uint32_t lo, uint32_t hi) {
-    const u32x2_t u = {lo, hi};
-    const bf16x4_t b = __builtin_bit_cast(bf16x4_t, u);
-    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(h, b, z, 0, 0, 0);
-}
 
 // A operands of v_mfma_f32_16x16x32_bf16 for a transform of five index bits
 // of 32 values: lane (j, g = lane / 16) holds k = 8 g + t (t = 0..7) of B
@@ -615,8 +580,8 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 // ----------------------------------------------------------------- k128
 // Eight rows of 128 per wave.  Lane l: n = l % 16, row = n >> 1, h = n & 1,
 // q = l >> 4; chunk c in {0, 1} holds row elements 64 c + 32 h + 8 q + r.
-// The MFMA transforms bits {0, 1, 3, 4}, registers bits 2 and 6, the DPP
-// butterfly bit 5.  The 128 elements of a row sit in the 8 lanes sharing n >> 1.
+// The MFMA (16x16x32, one 16-byte load as B) transforms bits {0..4},
+// registers bit 6, the DPP butterfly bit 5.  The 128 elements of a row sit in the 8 lanes sharing n >> 1.
 template <bool WROT, class Q0>
 __global__ void __launch_bounds__(256) k128(const FastArgs a) {
     const int lane = threadIdx.x & 63;
@@ -633,19 +598,22 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
     u32x4_t raw[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) raw[c] = ldg16(src + 64 * c);
-    const bf16x4_t hop = h16_operand(lane);
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);   // hp[64]: row half 1
+    const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
+    const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
     float v[16];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const f32x4_t d0 = mfma_h16(hop, raw[c][0], raw[c][1]);
-        const f32x4_t d1 = mfma_h16(hop, raw[c][2], raw[c][3]);
+        const bf16x8_t Bc = __builtin_bit_cast(bf16x8_t, raw[c]);
+        const f32x4v_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Bc, f32x4v_t{}, 0, 0, 0);
+        const f32x4v_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bc, f32x4v_t{}, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             v[8 * c + j] = d0[j];
             v[8 * c + 4 + j] = d1[j];
         }
     }
-    bfly<16, 0xCu>(v);                           // bits 2 (v-index bit 2) and 6 (v-index bit 3)
+    bfly<16, 0x8u>(v);                           // bit 6 (v-index bit 3)
     dpp_bfly<kXor1>(v, h ? -1.0f : 1.0f);        // bit 5
     const int64_t e0 = row * 128 + col0;
 
