@@ -28,16 +28,11 @@
 
 #include <atomic>
 
+#include "codes.h"
 #include "plan.h"
 
 namespace hr {
 namespace {
-
-__device__ __forceinline__ uint32_t f2bf_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
 
 template <int LOGB, int TB, bool BF16>
 __global__ void __launch_bounds__(1 << (TB - 5)) colrot_kernel(const ColArgs a) {
@@ -172,10 +167,10 @@ __global__ void __launch_bounds__(1 << (TB - 5)) colrot_kernel(const ColArgs a) 
             const int64_t e = o + r * a.in + cc;
             if constexpr (BF16) {
                 uint4 d;
-                d.x = f2bf_rne(v[0]) | (f2bf_rne(v[1]) << 16);
-                d.y = f2bf_rne(v[2]) | (f2bf_rne(v[3]) << 16);
-                d.z = f2bf_rne(v[4]) | (f2bf_rne(v[5]) << 16);
-                d.w = f2bf_rne(v[6]) | (f2bf_rne(v[7]) << 16);
+                d.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
+                d.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
+                d.z = f2bf(v[4]) | (f2bf(v[5]) << 16);
+                d.w = f2bf(v[6]) | (f2bf(v[7]) << 16);
                 *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.w_rot) + e) = d;
             } else {
                 float* dst = static_cast<float*>(a.w_rot) + e;

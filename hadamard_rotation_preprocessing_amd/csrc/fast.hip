@@ -26,6 +26,7 @@
 
 #include <atomic>
 
+#include "codes.h"
 #include "plan.h"
 
 namespace hr {
@@ -50,12 +51,6 @@ struct QD {
 };
 using QNone = QD<-1, 0, 0, 0>;
 
-__device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
 __device__ __forceinline__ u32x4_t ldg16(const void* p) {
     return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
@@ -1022,21 +1017,6 @@ __device__ __forceinline__ float max_quad16(float v) {
     return max_halves(v);
 }
 
-// E4M3 (OCP e4m3fn) byte of d >= 0: nearest, ties to the even mantissa,
-// saturating at 448.  From 2^-6 up, rounding the float32 pattern at mantissa
-// bit 20 leaves (biased exponent << 3 | three mantissa bits), and the byte is
-// that less (127 - 7) << 3; below 2^-6 the byte counts units of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_byte_f(float d) {
-    d = fminf(d, 448.0f);
-    const uint32_t u = __float_as_uint(d);
-    if (u >= 0x3C800000u) return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
-    return static_cast<uint32_t>(rintf(d * 512.0f));
-}
-
-__device__ __forceinline__ float e4m3_value_f(uint32_t b) {
-    return (b >> 3) ? __uint_as_float((b + 960u) << 20) : static_cast<float>(b) * 0.001953125f;
-}
-
 template <int LOGB, bool WROT, class Q0>
 __global__ void __launch_bounds__(256) kbsmall(const FastArgs a) {
     static_assert(LOGB == 4 || LOGB == 5, "blocks of 16 or 32");
@@ -1111,8 +1091,8 @@ __global__ void __launch_bounds__(256) kbsmall(const FastArgs a) {
             for (int r = 1; r < 8; ++r) am = fmaxf(am, fabsf(y[r]));
             am = fmaxf(am, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(am), 0x401F)));   // xor 16
             const float ts = a.q[0].tscale;
-            const uint32_t byte = e4m3_byte_f(am / (6.0f * ts));
-            const float sc = e4m3_value_f(byte) * ts;
+            const uint32_t byte = e4m3_byte(am / (6.0f * ts));
+            const float sc = e4m3_value(byte) * ts;
             const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
             float t[8];
 #pragma unroll
