@@ -305,8 +305,11 @@ def _oracle_mixed(x, n, block, m):
     (7, 4096, 0, torch.bfloat16, True, True, True, hr.QSpec("int", 4, 128, False, "bf16")),
     (9, 14336, 2048, torch.bfloat16, False, True, True, hr.QSpec("int", 4, 128, False, "bf16")),  # signs, odd blocks
     (6, 4096, 0, torch.bfloat16, False, True, False, hr.QSpec("int", 4, 128, True, "bf16")),
+    (40, 4096, 16, torch.bfloat16, True, True, False, hr.QSpec.nvfp4(0.02)),                    # RPBH + NV
+    (33, 4096, 0, torch.bfloat16, False, False, True, hr.QSpec.nvfp4()),                        # random H + NV
 ], ids=["random-full-bf16", "random-full-f32", "rpbh-256", "rpbh-32-mxfp4", "all-512", "all-kron96",
-        "rpbh-2048-r4", "perm-2048-sym", "all-4096-asym", "signs-2048-r4", "in-signs-4096"])
+        "rpbh-2048-r4", "perm-2048-sym", "all-4096-asym", "signs-2048-r4", "in-signs-4096",
+        "rpbh-16-nvfp4", "random-full-nvfp4"])
 def test_mixed_rotate_quantize(case):
     rows, n, block, dt, pm, si, so, spec = case
     x = synth.gaussian((rows, n), seed=14000 + n + block, dtype=dt)
@@ -541,6 +544,25 @@ def test_empty_tensor():
     assert y.shape == (0, 256)
     o = hr.rotate_quantize_act(x, 0, hr.QSpec("int", 4, 128, False, "bf16"))
     assert o["codes"].shape == (0, 128)
+    o = hr.rotate_quantize_act(x, 16, hr.QSpec.nvfp4(0.5))
+    assert o["codes"].shape == (0, 128) and o["scales"].shape == (0, 16)
+    w = hr.rotate_fuse_weight_out(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), 0)
+    assert w.shape == (0, 64)
+    torch.cuda.synchronize()
+
+
+def test_weight_fusion_nvfp4_and_mxfp4():
+    """Both FP4 forms of W . R from one read (the generic kernel takes two
+    quantizers of different group sizes)."""
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=40, in_features=2048)
+    specs = [hr.QSpec.nvfp4(), hr.QSpec.mxfp4()]
+    say("rotate_fuse_weight NVFP4 + MXFP4", tuple(w.shape))
+    out = hr.rotate_fuse_weight(w.to(DEV), 32, specs, w_rot=False)
+    torch.cuda.synchronize()
+    y = oracle.rotate(w, 2048, 32)
+    rep = Report()
+    check_nvfp4(out["quant"][0], y, rep)
+    check_mxfp4(out["quant"][1], y, rep)
 
 
 def test_errors_leave_outputs_untouched():
