@@ -130,7 +130,7 @@ def build_parts(hr, synth, torch, only):
     # output-side fusion W' = R1^T W on down_proj [4096, 14336] (full width
     # along out_features)
     if only is not None and "down_out" in only:
-        wd = synth.gaussian((4096, 14336), seed=104, dtype=torch.bfloat16).to(dev)
+        wd = synth.make_inputs(W["weight"], out_features=4096, in_features=14336).to(dev)
         yd = torch.empty_like(wd)
         parts["down_out"] = dict(fn=lambda wd=wd, yd=yd: hr.rotate_fuse_weight_out(wd, 0, out=yd),
                                  bytes=wd.numel() * 4, rows=wd.shape[0])

@@ -191,7 +191,7 @@ def test_block16_nvfp4_full_size(name):
 def test_down_proj_output_fusion_full_size():
     """rotate_fuse_weight_out on down_proj [4096, 14336] as bench.py times it,
     checked on sampled columns (each a full-length transform)."""
-    w = synth.gaussian((4096, 14336), seed=104, dtype=torch.bfloat16)
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=4096, in_features=14336)
     say("down_proj output fusion full size")
     wr = hr.rotate_fuse_weight_out(w.to(DEV), 0)
     torch.cuda.synchronize()
