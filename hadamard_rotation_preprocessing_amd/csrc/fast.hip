@@ -888,7 +888,7 @@ __device__ __forceinline__ void epi_kron(const float (&u)[64], float f, const Qu
 }
 
 template <int K, bool WROT, class Q0>
-__global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
+__global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
     static_assert(K <= 32, "one MFMA K-padding of 32");
     constexpr int M = 512;
     constexpr int n = K * M;
@@ -923,17 +923,18 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
         smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
     }
 
-    // Rows blockIdx.x, blockIdx.x + gridDim.x, ...: the next row's loads are
-    // in flight while the current row is transformed.
+    // Rows blockIdx.x, blockIdx.x + gridDim.x, ...  Each row is loaded just
+    // before it is staged: without a prefetch the kernel fits 128 VGPRs, so
+    // four workgroups per CU hide one another's load latency.
     int64_t row = blockIdx.x;
     const int64_t stride = gridDim.x;
     const int c = lane & 31;                   // piece
     const int g = lane >> 5;                   // column bit b6 after the mix
     const bool valid = c < K;
-    if (stager) load(row);
     for (;;) {
+        if (stager) load(row);
         // ---- phase 1: stage the row (16-byte slot of column 8 lane + cc at
-        // 8 lane + (cc ^ (lane & 7)) within octet w), then prefetch the next
+        // 8 lane + (cc ^ (lane & 7)) within octet w)
         if (stager) {
             const int base = 16 * (w * 512 + 8 * lane);     // bytes
             const int hs16 = 16 * (lane & 7);
@@ -947,7 +948,6 @@ __global__ void __launch_bounds__(256, 3) kkron(const KronArgs a) {
             }
         }
         const int64_t next = row + stride;
-        if (stager && next < a.rows) load(next);
         __syncthreads();
 
         // ---- phase 2: mix on the MFMA, six register stages, one across halves
