@@ -396,7 +396,9 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     // permutation: one workgroup per row of n <= 16384, staged in rowbuf, whose
     // space then holds the waves' transpose buffers
     constexpr int RB16 = 2 * 4 * KW::LDS > 16384 ? 2 * 4 * KW::LDS : 16384;   // uint16 words
-    __shared__ float lds_all[PERM ? 1 : 4][PERM ? 1 : KW::LDS];
+    // per-wave buffer: the transpose, plus (rotated output) the bf16 store staging
+    constexpr int LDSZ = WROT ? KW::LDS : KW::LDS_T;
+    __shared__ float lds_all[PERM ? 1 : 4][PERM ? 1 : LDSZ];
     __shared__ __attribute__((aligned(16))) uint16_t rowbuf[PERM ? RB16 : 8];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
