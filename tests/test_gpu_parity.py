@@ -475,6 +475,21 @@ def test_weight_out_fusion(shape):
     check_rotated(got.T.copy(), ref.T.copy(), dtname(w))
 
 
+@pytest.mark.parametrize("block", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+def test_weight_out_every_block(block):
+    """Every block size, with in_features three times the smallest tile width
+    (so the smallest tile of that block is taken) and two row blocks (one for
+    4096)."""
+    out_f = block * (1 if block == 4096 else 2)
+    in_f = 3 * max(8, 2048 // block)
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=out_f, in_features=in_f)
+    say("rotate_fuse_weight_out", out_f, in_f, block)
+    wr = hr.rotate_fuse_weight_out(w.to(DEV), block)
+    torch.cuda.synchronize()
+    ref = oracle.rotate_out(w, out_f, block)
+    check_rotated(to_np64(wr).T.copy(), ref.T.copy(), "bf16")
+
+
 def test_weight_out_in_place_and_layer_equivalence():
     """In place, and the fused weight reproduces the rotated layer output:
     x . W'^T against (x . W^T) . R on the GPU-rounded weight."""
