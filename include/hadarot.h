@@ -66,6 +66,11 @@
  *     returns the message of the last failing call on this thread.
  *   - rows == 0 is a valid empty tensor: the call returns HR_OK and enqueues
  *     nothing (pointers may then be NULL).
+ *   - Graph capture: apart from dequant_check with `stats`, a call enqueues
+ *     kernel launches only (no allocation, copy or memset), so it may be
+ *     captured in a HIP graph and replayed.  The first call for a kernel on a
+ *     device also queries the device's occupancy on the host; making one call
+ *     before capturing keeps that query out of the capture (the tested use).
  */
 #ifndef HADAROT_H
 #define HADAROT_H

@@ -728,3 +728,60 @@ def test_int4_exact_ties(kernel_path):
     codes = oracle.unpack_nibbles(out["codes"].cpu().numpy().reshape(-1), y.size, signed=True).reshape(y.shape)
     assert np.array_equal(to_np64(out["scales"]).reshape(ref.scales.shape), ref.scales)
     assert np.array_equal(codes, ref.codes)
+
+
+# ------------------------------------------------------------ graph capture
+
+@pytest.mark.parametrize("path", ["kwave-int4", "kkron", "kbsmall-nvfp4", "colrot", "weight-two-specs"])
+def test_hip_graph_capture_replays_match_eager(path):
+    """The entry points allocate nothing and enqueue only kernels, so they can
+    be captured in a HIP graph: three replays, each after the input changed
+    in place (eager work between the replays), match eager calls bit for bit."""
+    torch.manual_seed(0)
+    if path == "kwave-int4":
+        x = synth.gaussian((64, 4096), seed=61, dtype=torch.bfloat16).to(DEV)
+        spec = hr.QSpec("int", 4, 128, False, "bf16")
+        out = hr.alloc_quant_outputs(64, 4096, spec, DEV)
+        run = lambda: hr.rotate_quantize_act(x, 0, spec, out=out)
+        snap = lambda: [out["codes"].clone(), out["scales"].clone(), out["zeros"].clone()]
+    elif path == "kkron":
+        x = synth.gaussian((16, 14336), seed=62, dtype=torch.bfloat16).to(DEV)
+        spec = hr.QSpec("int", 4, 128, False, "bf16")
+        out = hr.alloc_quant_outputs(16, 14336, spec, DEV)
+        run = lambda: hr.rotate_quantize_act(x, 0, spec, out=out)
+        snap = lambda: [out["codes"].clone(), out["scales"].clone(), out["zeros"].clone()]
+    elif path == "kbsmall-nvfp4":
+        x = synth.gaussian((64, 4096), seed=63, dtype=torch.bfloat16).to(DEV)
+        spec = hr.QSpec.nvfp4(0.25)
+        out = hr.alloc_quant_outputs(64, 4096, spec, DEV)
+        run = lambda: hr.rotate_quantize_act(x, 16, spec, out=out)
+        snap = lambda: [out["codes"].clone(), out["scales"].clone()]
+    elif path == "colrot":
+        x = synth.gaussian((4096, 256), seed=64, dtype=torch.bfloat16).to(DEV)
+        y = torch.empty_like(x)
+        run = lambda: hr.rotate_fuse_weight_out(x, 0, out=y)
+        snap = lambda: [y.clone()]
+    else:
+        x = synth.gaussian((48, 4096), seed=65, dtype=torch.bfloat16).to(DEV)
+        specs = [hr.QSpec.mxfp4(), hr.QSpec("int", 4, 128, True, "bf16")]
+        wo = {"w_rot": torch.empty_like(x), "quant": [hr.alloc_quant_outputs(48, 4096, s, DEV) for s in specs]}
+        run = lambda: hr.rotate_fuse_weight(x, 0, specs, out=wo)
+        snap = lambda: [wo["w_rot"].clone()] + [t.clone() for q in wo["quant"] for t in (q["codes"], q["scales"])]
+    say("graph capture", path)
+    run()                                   # first call outside capture (one-time launch setup)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        x.mul_(-1.5 if i % 2 else 0.75)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        run()                               # eager reference on the same input
+        torch.cuda.synchronize()
+        want = snap()
+        for a_, b_ in zip(got, want):
+            assert torch.equal(a_, b_), (path, i)
