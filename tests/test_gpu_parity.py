@@ -162,6 +162,28 @@ def test_block_diagonal_rotate_quant(block):
     run_act(x, n, block, hr.QSpec("int", 4, 128, False, "bf16"), y_rot=True)
 
 
+@pytest.mark.parametrize("case", [(32768, 8192, "int-asym"), (32768, 16384, "int-sym"), (16384, 0, "nvfp4"),
+                                  (30720, 0, "int-asym"), (30720, 0, "mxfp4")],
+                         ids=["b8192", "b16384", "full-16384-nvfp4", "kron60x512", "kron60x512-mxfp4"])
+def test_maximum_widths(case):
+    """The widest supported rows: n = 32768 with large blocks, NVFP4's widest
+    block (1024 groups of 16), and the largest Kronecker width 60 x 512 (the
+    generic kernel)."""
+    n, block, q = case
+    x = synth.gaussian((5, n), seed=5100 + n + block, dtype=torch.bfloat16)
+    x[3] *= 1e-3
+    spec = {"int-asym": hr.QSpec("int", 4, 128, False, "bf16"), "int-sym": hr.QSpec("int", 4, 64, True, "f32"),
+            "nvfp4": hr.QSpec.nvfp4(), "mxfp4": hr.QSpec.mxfp4()}[q]
+    run_act(x, n, block, spec, y_rot=True)
+
+
+def test_block_beyond_1024_groups_is_unsupported():
+    x = synth.gaussian((3, 32768), seed=5200, dtype=torch.bfloat16).to(DEV)
+    with pytest.raises(hr.HadarotError) as e:
+        hr.rotate_quantize_act(x, 0, hr.QSpec.nvfp4())
+    assert e.value.status == hr.L.HR_EUNSUPPORTED and "1024" in str(e.value)
+
+
 @pytest.mark.parametrize("block", [128, 2048, 4096])
 @pytest.mark.parametrize("sym", [True, False])
 @pytest.mark.parametrize("y_rot", [False, True])
