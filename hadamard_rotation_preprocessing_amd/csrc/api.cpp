@@ -182,10 +182,13 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
         while (chunk < 16 && n % (2 * chunk) == 0) chunk *= 2;
     }
     // elements per thread: at most 16 (32 when a chunk needs it), at most
-    // the smallest group and the chunk
+    // the chunk, and at most the smallest group unless that needs more than
+    // 1024 threads
     int64_t e = 16;
     if (chunk / e > 1024) e = 32;
-    if (nq && gmin < e) e = gmin;
+    // one group per thread where that fits 1024 threads; else several whole
+    // groups per thread (INT and NVFP4 groups smaller than e)
+    if (nq && gmin < e && chunk / gmin <= 1024) e = gmin;
     if (chunk < e) e = chunk;
     if (e < 2) e = 2;
     if (chunk % e) return fail(HR_EUNSUPPORTED, "chunk of %lld elements is not a multiple of %lld",
@@ -212,7 +215,13 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     const int64_t wg_elems = nt * e;
     size_t lds = static_cast<size_t>(wg_elems + (wg_elems >> 4)) * 4;  // padded transform buffer
     lds += static_cast<size_t>(2 * (nt / 64 + 1)) * 4;                  // cross-wave reduction
-    if (nq) lds += static_cast<size_t>(wg_elems / gmin) * 4;           // zero-point staging
+    // zero-point staging: asymmetric groups at least a thread wide (smaller
+    // groups are whole in one thread, which writes their zero points itself)
+    int64_t zgroups = 0;
+    for (int i = 0; i < nq; ++i)
+        if (qs[i].format == HR_Q_INT && !qs[i].sym && qs[i].g >= e && wg_elems / qs[i].g > zgroups)
+            zgroups = wg_elems / qs[i].g;
+    lds += static_cast<size_t>(zgroups) * 4;
     if (lds > 160 * 1024) return fail(HR_EUNSUPPORTED, "needs %zu bytes of LDS", lds);
     p->lds_bytes = lds;
     hr::RotArgs& a = p->a;

@@ -238,11 +238,114 @@ __device__ __forceinline__ void kron_mix(float (&v)[1 << LOGE], float* lds, int 
 
 // ---------------------------------------------------------------- epilogue
 
+// Several whole groups of G = 2^LOGG elements in one thread's E = 2^LOGE
+// (LOGG < LOGE): blocks wider than 1024 groups.  INT and NVFP4 (MXFP4's
+// groups of 32 are never smaller than a thread's elements).  Every group is
+// the thread's own, so nothing is exchanged and no barrier is needed.
+template <int LOGE, int LOGG>
+__device__ __forceinline__ void quantize_multi(const float (&y)[1 << LOGE], const QuantDev& q, bool valid,
+                                               int64_t e0) {
+    constexpr int E = 1 << LOGE, G = 1 << LOGG, NG = E / G;
+    static_assert(NG >= 2 && E >= 8, "several groups, whole bytes of codes");
+    const int64_t G0 = e0 >> LOGG;   // even: e0 is a multiple of E >= 2 G
+    uint32_t w[E / 8];
+#pragma unroll
+    for (int k = 0; k < E / 8; ++k) w[k] = 0u;
+    uint32_t zq[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        float r0 = y[k * G], r1 = -y[k * G];   // max y, max(-y)
+#pragma unroll
+        for (int j = 1; j < G; ++j) {
+            r0 = fmaxf(r0, y[k * G + j]);
+            r1 = fmaxf(r1, -y[k * G + j]);
+        }
+        zq[k] = 0u;
+        if (q.format == 2) {
+            const uint32_t byte = e4m3_byte(fmaxf(r0, r1) / (6.0f * q.tscale));
+            const float s = e4m3_value(byte) * q.tscale;
+            if (s > 0.0f) {
+                const float inv = 1.0f / s;
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const int jj = k * G + j;
+                    const float a = fabsf(y[jj] * inv);
+                    uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                                   (a >= 3.5f) + (a > 5.0f);
+                    idx |= (y[jj] < 0.0f) ? 8u : 0u;
+                    w[jj >> 3] |= idx << (4 * (jj & 7));
+                }
+            }
+            if (valid) static_cast<uint8_t*>(q.scales)[G0 + k] = static_cast<uint8_t>(byte);
+        } else {
+            float s = q.sym ? fmaxf(r0, r1) / 7.0f : (fmaxf(r0, 0.0f) + fmaxf(r1, 0.0f)) / 15.0f;
+            uint32_t sbits = 0;
+            if (q.scale_dtype == 1) {
+                sbits = f2bf(s);
+                s = bf2f(sbits);
+                if (s == 0.0f) {
+                    s = 1.0f;
+                    sbits = 0x3F80u;
+                }
+            } else if (s == 0.0f) {
+                s = 1.0f;
+            }
+            const float inv = 1.0f / s;
+            float zf = 0.0f;
+            if (!q.sym) zf = fminf(fmaxf(rintf(fmaxf(r1, 0.0f) / s), 0.0f), 15.0f);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int jj = k * G + j;
+                uint32_t c;
+                if (q.sym) {
+                    const float t = fminf(fmaxf(rintf(y[jj] * inv), -8.0f), 7.0f);
+                    c = static_cast<uint32_t>(static_cast<int>(t)) & 0xFu;
+                } else {
+                    const float t = fminf(fmaxf(rintf(y[jj] * inv) + zf, 0.0f), 15.0f);
+                    c = static_cast<uint32_t>(static_cast<int>(t));
+                }
+                w[jj >> 3] |= c << (4 * (jj & 7));
+            }
+            zq[k] = static_cast<uint32_t>(static_cast<int>(zf));
+            if (valid) {
+                if (q.scale_dtype == 1)
+                    static_cast<uint16_t*>(q.scales)[G0 + k] = static_cast<uint16_t>(sbits);
+                else
+                    static_cast<float*>(q.scales)[G0 + k] = s;
+            }
+        }
+    }
+    if (valid && q.format == 0 && !q.sym) {
+#pragma unroll
+        for (int k = 0; k < NG; k += 2) q.zeros[(G0 + k) >> 1] = static_cast<uint8_t>((zq[k] & 0xFu) | ((zq[k + 1] & 0xFu) << 4));
+    }
+    if (valid) store_codes<E>(q.codes, e0, w);
+}
+
+template <int LOGE>
+__device__ __forceinline__ void quantize_multi_any(const float (&y)[1 << LOGE], const QuantDev& q, bool valid,
+                                                   int64_t e0) {
+    if constexpr (LOGE >= 4) {
+        switch (q.logg) {
+            case 1: quantize_multi<LOGE, 1>(y, q, valid, e0); break;
+            case 2: quantize_multi<LOGE, 2>(y, q, valid, e0); break;
+            case 3: quantize_multi<LOGE, 3>(y, q, valid, e0); break;
+            default:
+                if constexpr (LOGE >= 5) quantize_multi<LOGE, 4>(y, q, valid, e0);
+                break;
+        }
+    }
+}
+
 template <int LOGE>
 __device__ __forceinline__ void quantize(const float (&y)[1 << LOGE], const QuantDev& q, int64_t total_groups,
                                          int tid, int nt, bool valid, int64_t e0, int64_t wg_e0,
                                          float* red, int* zst) {
     constexpr int E = 1 << LOGE;
+    if (q.logg < LOGE) {           // several groups per thread (uniform over the workgroup)
+        quantize_multi_any<LOGE>(y, q, valid, e0);
+        return;
+    }
     const int gl = q.logg - LOGE;  // log2(threads per group), >= 0
     const int gth = 1 << gl;
 

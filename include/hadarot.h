@@ -161,9 +161,6 @@ int hadamard_rotate(const void* x, void* y, int dtype, int64_t rows, int64_t n,
  *          else must be NULL.
  *   y_rot  device or NULL: if set, also writes the rotated tensor in `dtype`
  *          (may equal x).
- * A rotation block (the full width n when block <= 0) may hold at most 1024
- * groups of the smallest group size: e.g. 16384 elements for NVFP4's groups
- * of 16.  Larger ones return HR_EUNSUPPORTED (so does rotate_fuse_weight).
  */
 int rotate_quantize_act(const void* x, int dtype, int64_t rows, int64_t n, int64_t block,
                         const hr_qspec* q, void* codes, void* scales, void* zeros,

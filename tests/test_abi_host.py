@@ -85,7 +85,6 @@ def msg():
     (dict(n=4097 * 2, block=0, qs=q(g=2)), L.HR_EUNSUPPORTED, "base Hadamard"),
     (dict(n=65536, block=0), L.HR_EUNSUPPORTED, "exceeds"),
     (dict(n=131072, block=65536), L.HR_EUNSUPPORTED, "exceeds 32768"),
-    (dict(n=4096, block=4096, qs=q(g=2)), L.HR_EUNSUPPORTED, "1024 threads"),
     (dict(n=128 * 108, block=0), L.HR_EUNSUPPORTED, "exceeds 64"),
 ])
 def test_rotate_quantize_act_validation(kw, status, text):

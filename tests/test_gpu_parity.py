@@ -177,11 +177,34 @@ def test_maximum_widths(case):
     run_act(x, n, block, spec, y_rot=True)
 
 
-def test_block_beyond_1024_groups_is_unsupported():
-    x = synth.gaussian((3, 32768), seed=5200, dtype=torch.bfloat16).to(DEV)
-    with pytest.raises(hr.HadarotError) as e:
-        hr.rotate_quantize_act(x, 0, hr.QSpec.nvfp4())
-    assert e.value.status == hr.L.HR_EUNSUPPORTED and "1024" in str(e.value)
+@pytest.mark.parametrize("case", [(32768, 0, hr.QSpec.nvfp4(0.5)), (16384, 16384, hr.QSpec("int", 4, 8, True, "bf16")),
+                                  (8192, 8192, hr.QSpec("int", 4, 4, False, "f32")),
+                                  (32768, 32768, hr.QSpec("int", 4, 2, False, "bf16")),
+                                  (4096, 4096, hr.QSpec("int", 4, 2, True, "f32"))],
+                         ids=["full-32768-nvfp4", "b16384-int-g8", "b8192-asym-g4", "b32768-asym-g2", "b4096-g2"])
+def test_more_than_1024_groups_per_block(case):
+    """Blocks of more than 1024 groups: each thread of the generic kernel
+    quantizes several whole groups (asymmetric zero points written per
+    thread)."""
+    n, block, spec = case
+    x = synth.gaussian((3, n), seed=5200 + n + spec.group_size, dtype=torch.bfloat16)
+    x[1, : n // 3] = 0.0
+    run_act(x, n, block, spec, y_rot=True)
+
+
+def test_weight_fusion_two_group_sizes_wide():
+    """Two quantizers on a 32768-wide weight: groups of 128 spread over four
+    threads and NVFP4 groups of 16, two per thread, from one read."""
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=6, in_features=32768)
+    specs = [hr.QSpec("int", 4, 128, True, "bf16"), hr.QSpec.nvfp4()]
+    say("rotate_fuse_weight 32768 wide, INT g128 + NVFP4")
+    out = hr.rotate_fuse_weight(w.to(DEV), 0, specs)
+    torch.cuda.synchronize()
+    y = oracle.rotate(w, 32768)
+    rep = Report()
+    check_rotated(to_np64(out["w_rot"]), y, "bf16", rep)
+    check_int(out["quant"][0], y, 128, True, "bf16", rep)
+    check_nvfp4(out["quant"][1], y, rep)
 
 
 @pytest.mark.parametrize("block", [128, 2048, 4096])
