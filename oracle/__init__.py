@@ -31,7 +31,6 @@ from .hadamard import (  # noqa: F401
     rotate_out,
     rotation_matrix,
     sylvester,
-    sylvester_entry,
 )
 from .quant import (  # noqa: F401
     E2M1_VALUES,

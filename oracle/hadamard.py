@@ -51,11 +51,6 @@ def sylvester(n: int) -> np.ndarray:
     return h
 
 
-def sylvester_entry(i: int, j: int) -> int:
-    """Closed form of the Sylvester entry: (-1)^popcount(i & j)."""
-    return -1 if bin(i & j).count("1") % 2 else 1
-
-
 # ------------------------------------------------------- finite fields, Paley
 
 def _prime_power(q: int):

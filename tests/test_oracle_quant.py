@@ -13,6 +13,7 @@ force over every E4M3 and E2M1 value.
 import json
 import math
 import os
+import struct
 from fractions import Fraction
 
 import numpy as np
@@ -53,6 +54,49 @@ def test_bf16_round_direct_from_float64_no_double_rounding():
     # other side.  Direct rounding gives 1.0.
     assert Q.bf16_round(1.0 + 2.0 ** -8 - 2.0 ** -40) == 1.0
     assert Q.bf16_round(1.0 + 3 * 2.0 ** -8 - 2.0 ** -40) == 1.0 + 2.0 ** -7
+
+
+def _f32_c(v: float) -> float:
+    """float64 -> float32 by the C library's conversion (struct), an
+    implementation independent of numpy's."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def test_fp32_round_ties_to_even_and_direction():
+    one = 1.0
+    u = 2.0 ** -23                                         # float32 ulp at 1
+    assert Q.fp32_round(one + u / 2) == 1.0                # tie, 1.0 is even
+    assert Q.fp32_round(one + 3 * u / 2) == one + 2 * u    # tie, goes up to even
+    assert Q.fp32_round(one + u / 2 + 2.0 ** -50) == one + u   # above the midpoint
+    assert Q.fp32_round(one + u / 2 - 2.0 ** -50) == 1.0       # below it
+    assert Q.fp32_round(-(one + 3 * u / 2)) == -(one + 2 * u)  # sign symmetric
+    assert Q.fp32_round(one + 0.75 * u) == one + u         # nearest, not toward zero
+    assert Q.fp32_round(-(one + 0.75 * u)) == -(one + u)
+
+
+def test_fp32_round_matches_torch_and_c_at_midpoints():
+    """Exact float32 midpoints (ties) and points just beside them, compared
+    with torch's float64 -> float32 conversion and the C library's."""
+    rng = np.random.default_rng(5)
+    a = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    a = a[np.isfinite(a) & (np.abs(a) > 1e-30)].astype(np.float64)
+    b = np.nextafter(a.astype(np.float32), np.float32(np.inf)).astype(np.float64)
+    mid = 0.5 * (a + b)                    # exact in float64
+    vals = np.concatenate([mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf), a])
+    ours = Q.fp32_round(vals)
+    ref = torch.from_numpy(vals).to(torch.float32).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+    for i in range(0, vals.size, 97):
+        assert ours[i] == _f32_c(float(vals[i]))
+
+
+def test_fp32_scales_of_hand_cases_are_exact():
+    """The stored float32 scales of the hand-worked cases equal the C library's
+    float32 of 5/7 and 7/15 exactly (not merely within a tolerance)."""
+    r = oracle.rtn_quant(np.array([[5.0, -1.0, -2.0, 0.0]]), 4, 4, True, "f32")
+    assert r.scales[0, 0] == _f32_c(5.0 / 7.0)
+    r = oracle.rtn_quant(np.array([[5.0, -1.0, -2.0, 0.0]]), 4, 4, False, "f32")
+    assert r.scales[0, 0] == _f32_c(7.0 / 15.0)
 
 
 # --------------------------------------------------------------------- RTN
