@@ -12,6 +12,10 @@ seeded synthetic input already resident in HBM:
   r3_k     R3 keys (same shape): FWHT 128 + int4 asym per head vector
   weight   W 14336 x 4096 bf16 -> W.H bf16 + MXFP4 + int4 sym g128, one read
 
+Reported beside the step (not part of it): tiny, 256 x 128 float32 with
+FWHT 128, int4 sym g32 and the rotated float32 output; its 282,624 bytes take
+35 ns at HBM peak, so its launch time measures latency, not bandwidth.
+
 Measured only when named in --only (not part of the step): r1_mx32 and
 r4_mx32, the R1 and R4 inputs with a block-32 rotation fused with MXFP4
 (E2M1 codes, one E8M0 scale per block of 32); r1_nv16 and r4_nv16, the same
@@ -21,8 +25,10 @@ random Hadamard H diag(+-1); r4_rpbh, the R4 part with RPBH (permutation,
 signs, blocks of 2048); down_out, the output-side fusion R1^T W on down_proj
 [4096, 14336].
 
-The step touches about 2 GB, eight times the 256 MB Infinity Cache, so every
-launch reads its input from HBM.  Timing uses HIP events on the stream the
+The step touches about 2 GB, eight times the 256 MB Infinity Cache, and no
+two launches read the same tensor, so every launch reads its input from HBM.
+Warm-up runs at least --warmup steps and at least --min-warmup-s seconds
+(both reported).  Timing uses HIP events on the stream the
 kernels are launched on (torch's current stream).  The value is algorithmic
 bytes (one read of each input plus every mandatory output write) per second
 over K whole steps with no event between launches; the per-part durations
@@ -146,8 +152,11 @@ def build_parts(hr, synth, torch, only):
                                bytes=b, rows=x.shape[0])
             host["r4"] = (x, w.n, 2048, [spec], False)
         if want("r4_kron"):
+            # its own copy of the input: right after r4, reads of r4's tensor
+            # could still hit the 256 MB Infinity Cache
+            xk = xg.clone()
             out2 = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts["r4_kron"] = dict(fn=lambda xg=xg, out=out2, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out2),
+            parts["r4_kron"] = dict(fn=lambda xk=xk, out=out2, spec=spec: hr.rotate_quantize_act(xk, 0, spec, out=out2),
                                     bytes=b, rows=x.shape[0])
             host["r4_kron"] = (x, w.n, 0, [spec], False)
     if want("r3_q") or want("r3_k"):
@@ -217,6 +226,33 @@ def cpu_baseline(host, fraction):
                       "float64 dense-matrix oracle, %.1f s wall" % (fraction, total_bytes, dt)}
 
 
+def time_tiny(hr, synth, torch, stream, launches):
+    """The tiny workload (256 x 128 float32, FWHT 128, int4 sym g32, rotated
+    float32 written), timed alone with an event pair per launch.  It moves
+    282,624 bytes, which HBM would carry in 35 ns: a launch takes microseconds,
+    so the figure measures launch latency, not bandwidth (reported outside
+    the step)."""
+    w = synth.WORKLOADS["tiny"]
+    x = synth.make_inputs(w).to("cuda:0")
+    spec = hr.QSpec.from_dict(w.qspecs[0])
+    out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, "cuda:0")
+    out["y_rot"] = torch.empty_like(x)
+    for _ in range(5):
+        hr.rotate_quantize_act(x, 0, spec, y_rot=True, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record(stream)
+        hr.rotate_quantize_act(x, 0, spec, y_rot=True, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    nbytes = x.numel() * 4 * 2 + qbytes(x.shape[0], w.n, spec)
+    return {"ms_median": round(med, 5), "ms_min": round(ms[0], 5), "bytes": nbytes,
+            "GB_s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "rows_per_s": round(x.shape[0] / (med * 1e-3), 1), "latency_bound": True}
+
+
 def traffic_for(kernel: str, digest: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources."""
@@ -237,6 +273,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="keep warming up (untimed steps) until this much wall time has passed")
     ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling), or of %s (block-32 MXFP4 "
                          "on the R1 / R4 inputs)" % (",".join(PARTS), ",".join(EXTRA_PARTS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -264,10 +302,21 @@ def main():
     print("inputs ready in %.1f s: %s" % (time.perf_counter() - t_gen, ", ".join(parts)), file=sys.stderr, flush=True)
     names = [p for p in PARTS + EXTRA_PARTS if p in parts]
 
-    for _ in range(args.warmup):
+    # warm-up: the W steps asked for, then more untimed steps until at least
+    # MIN_WARMUP_S of wall time has passed.  Right after idle the first ~10 ms
+    # of steps ran about 12 % slower (measured: 0.40 ms/step over 20 steps
+    # after a 2 ms warm-up, 0.36 ms/step after a longer one), so a short
+    # step-count warm-up alone would time that ramp, not the kernels.
+    t_w = time.perf_counter()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         for nm in names:
             parts[nm]["fn"]()
+        warm_steps += 1
+        if warm_steps >= args.warmup and warm_steps % 8 == 0:
+            torch.cuda.synchronize()   # at most 8 steps queued ahead of the GPU
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
 
     # the timed region: K whole steps, nothing recorded between launches
     stream = torch.cuda.current_stream()
@@ -293,6 +342,9 @@ def main():
             parts[nm]["fn"]()
             b.record(stream)
     torch.cuda.synchronize()
+    tiny = None
+    if only is None:
+        tiny = time_tiny(hr, synth, torch, stream, max(args.steps, 20))
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -318,12 +370,14 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "warmup": args.warmup, "warmup_steps_run": warm_steps, "warmup_s": round(warm_s, 3),
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic: seeded tensors shaped like 8B-class layers (no real activations or weights)",
         "config": {"workload": "hot-path step: " + " + ".join(names), "bytes_per_step": step_bytes,
                    "rows_per_step": step_rows, "io": "bf16 in; int4/MXFP4 codes, bf16 scales/outputs",
-                   "parts": per},
+                   "parts": per, "sum_of_parts_ms": round(sum(per[nm]["ms"] for nm in names), 5),
+                   "tiny": tiny},
         "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -27,7 +27,7 @@ from . import _lib as L
 from ._lib import HadarotError, check, lib  # noqa: F401
 
 __all__ = ["QSpec", "rotate", "rotate_quantize_act", "rotate_fuse_weight", "rotate_fuse_weight_out", "dequant_check",
-           "hadamard_rotate", "kron_order", "HadarotError", "alloc_quant_outputs"]
+           "hadamard_rotate", "kron_order", "check_shape", "set_generic_only", "HadarotError", "alloc_quant_outputs"]
 
 _SCALE_CODES = {"f32": L.HR_F32, "bf16": L.HR_BF16, "e8m0": L.HR_E8M0, "e4m3": L.HR_E4M3}
 _SCALE_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e8m0": torch.uint8, "e4m3": torch.uint8}
@@ -201,14 +201,29 @@ def dequant_check(q: dict, qspec: QSpec, rows: int, n: int, ref: torch.Tensor | 
     st = L.hr_dq_stats()
     spec = qspec.c()
     ref_dt = _dt(ref) if ref is not None else L.HR_F32
+    work = torch.empty(L.HR_DQ_WORK_BYTES, dtype=torch.uint8, device=dev) if want_stats else None
     check(lib().dequant_check(_ptr(codes), _ptr(q["scales"]), _ptr(q.get("zeros")),
                               ctypes.byref(spec), rows, n, _ptr(ref), ref_dt, _ptr(deq),
-                              ctypes.byref(st) if want_stats else None, _stream(codes)))
+                              ctypes.byref(st) if want_stats else None, _ptr(work), _stream(codes)))
     stats = None
     if want_stats:
         stats = dict(max_err_steps=st.max_err_steps, n_over_half_step=st.n_over_half_step,
                      n_clamped=st.n_clamped, rel_l2_err=st.rel_l2_err)
     return deq, stats
+
+
+def check_shape(dtype: torch.dtype, rows: int, n: int, block: int, qspecs=()) -> None:
+    """Raise HadarotError if the library does not implement this shape and
+    quantizer specs (host-only planning: nothing is allocated or launched)."""
+    qspecs = list(qspecs)
+    dt = {torch.float32: L.HR_F32, torch.bfloat16: L.HR_BF16}[dtype]
+    specs = (L.hr_qspec * max(1, len(qspecs)))(*[q.c() for q in qspecs])
+    check(lib().hr_check_shape(dt, rows, n, block, specs, len(qspecs)))
+
+
+def set_generic_only(on: bool) -> None:
+    """Route every later call through the generic kernel (testing aid)."""
+    lib().hr_set_generic_only(1 if on else 0)
 
 
 def kron_order(n: int, with_matrix: bool = False):

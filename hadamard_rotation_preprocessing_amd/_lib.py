@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libhadarot.so")
+# HADAROT_LIBRARY selects another build of the same ABI (the host-only
+# sanitizer build of the validation layer used by the CPU tests)
+LIB_PATH = os.environ.get("HADAROT_LIBRARY") or os.path.join(_PKG, "lib", "libhadarot.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_EDEVICE = 0, -1, -2, -3
 HR_F32, HR_BF16, HR_E8M0, HR_E4M3 = 0, 1, 2, 3
@@ -19,7 +21,8 @@ HR_Q_INT, HR_Q_MXFP4, HR_Q_NVFP4 = 0, 1, 2
 EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
            "dequant_check", "hr_last_error", "hr_kron_order",
            "hadamard_rotate_mixed", "rotate_quantize_act_mixed", "rotate_fuse_weight_mixed",
-           "rotate_fuse_weight_out")
+           "rotate_fuse_weight_out", "hr_check_shape", "hr_set_generic_only")
+HR_DQ_WORK_BYTES = 65536
 
 
 class hr_qspec(ctypes.Structure):
@@ -71,7 +74,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(hr_qout), vp]
         L.rotate_fuse_weight.restype = ci
         L.dequant_check.argtypes = [vp, vp, vp, ctypes.POINTER(hr_qspec), i64, i64, vp, ci, vp,
-                                    ctypes.POINTER(hr_dq_stats), vp]
+                                    ctypes.POINTER(hr_dq_stats), vp, vp]
         L.dequant_check.restype = ci
         L.hr_last_error.argtypes = []
         L.hr_last_error.restype = ctypes.c_char_p
@@ -88,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.rotate_fuse_weight_mixed.restype = ci
         L.rotate_fuse_weight_out.argtypes = [vp, ci, i64, i64, i64, vp, vp]
         L.rotate_fuse_weight_out.restype = ci
+        L.hr_check_shape.argtypes = [ci, i64, i64, i64, ctypes.POINTER(hr_qspec), ci]
+        L.hr_check_shape.restype = ci
+        L.hr_set_generic_only.argtypes = [ci]
+        L.hr_set_generic_only.restype = None
         _lib = L
     return _lib
 

@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -50,16 +51,21 @@ def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     obj_dir = os.path.join(LIBDIR, "obj")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = []
     sources = [("kernels.hip", True), ("fast.hip", True), ("colrot.hip", True), ("api.cpp", False), ("paley.cpp", False)]
+    cmds, objs = [], []
     for src, device in sources:
         out = os.path.join(obj_dir, src + ".o")
         cmd = [hipcc, "-c"] + (["-x", "hip"] if device else []) + [os.path.join(CSRC, src), "-o", out]
         cmd += COMMON + ["--offload-arch=" + ARCH]
         if device:
             cmd += DEVICE_FLAGS
-        _run(cmd, verbose)
+        cmds.append(cmd)
         objs.append(out)
+    # the sources are independent: compile them side by side
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)

@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -193,16 +194,31 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     if (e < 2) e = 2;
     if (chunk % e) return fail(HR_EUNSUPPORTED, "chunk of %lld elements is not a multiple of %lld",
                                 (long long)chunk, (long long)e);
-    const int64_t tpc = chunk / e;
-    if (tpc > 1024)
+    if (chunk / e > 1024)
         return fail(HR_EUNSUPPORTED, "%lld elements per chunk need more than 1024 threads "
                     "(group_size %lld too small for this block)", (long long)chunk, (long long)gmin);
     if (geo.kron_k && e < 8)
         return fail(HR_EUNSUPPORTED, "Kronecker rotation needs group_size >= 8");
+    // several whole groups per thread are quantized by instances for 16 and
+    // 32 elements per thread only (groups of 2..8, or 2..16)
+    for (int i = 0; i < nq; ++i)
+        if (qs[i].g < e && e != 16 && e != 32)
+            return fail(HR_EUNSUPPORTED, "group_size %lld is smaller than the %lld elements per thread",
+                        (long long)qs[i].g, (long long)e);
+    int64_t tpc = chunk / e;
     int64_t cpw = tpc >= 256 ? 1 : 256 / tpc;
     for (int i = 0; i < nq; ++i)
         if (qs[i].format == HR_Q_INT && !qs[i].sym && (cpw * chunk / qs[i].g) % 2) asym_one_group = true;
-    if (asym_one_group) cpw *= 2;  // zero points are packed two groups per byte
+    // zero points are packed two groups per byte, so a workgroup holds an even
+    // number of groups: chunks of one asymmetric group are taken in pairs.
+    // Where a pair would need more than 1024 threads, each thread takes 32
+    // elements instead of 16 (groups are whole threads: g >= e).
+    if (asym_one_group && 2 * cpw * tpc > 1024 && e == 16 && chunk % 32 == 0) {
+        e = 32;
+        tpc = chunk / e;
+        cpw = tpc >= 256 ? 1 : 256 / tpc;
+    }
+    if (asym_one_group) cpw *= 2;
     const int64_t nt = cpw * tpc;
     if (nt > 1024) return fail(HR_EUNSUPPORTED, "workgroup of %lld threads needed", (long long)nt);
     const int64_t total_elems = rows * n;
@@ -258,12 +274,15 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
 // 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
 // Kronecker row of K x 512) take the call when one is compiled for its exact
 // shape (randomised rotations: kwave); the generic kernel runs
-// otherwise, or always when HADAROT_FORCE_GENERIC=1.
+// otherwise, or always after hr_set_generic_only(1).
+// Process-wide dispatch switch (hr_set_generic_only): 1 sends every call to
+// the generic kernel, so that tests can run each shape through both paths.
+std::atomic<int> g_generic_only{0};
+
 int run(const hr::RotPlan& p, void* stream) {
     if (p.grid == 0) return ok();
     const hr::RotArgs& a = p.a;
-    const char* force = getenv("HADAROT_FORCE_GENERIC");
-    const bool generic_only = force && force[0] == '1';
+    const bool generic_only = g_generic_only.load(std::memory_order_relaxed) != 0;
     const bool mixed = a.perm || a.in_signs || a.out_signs;
     // the specialised kernels read the sign vectors 8 and 16 bytes at a time
     const bool signs_aligned =
@@ -628,13 +647,16 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
 }
 
 int dequant_check(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
-                  int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* stream) {
+                  int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* work,
+                  void* stream) {
+    static_assert(hr::kDqWorkBytes <= HR_DQ_WORK_BYTES, "dequant_check workspace");
     int st = check_shape(HR_F32, rows, n);
     if (st) return st;
     QSpec qs;
     if ((st = check_qspec(q, n, &qs))) return st;
     if (!deq && !stats) return fail(HR_EINVAL, "nothing to compute: deq and stats are NULL");
     if (stats && !ref) return fail(HR_EINVAL, "stats requires ref");
+    if (stats && !work) return fail(HR_EINVAL, "stats requires work (HR_DQ_WORK_BYTES of device memory)");
     if (ref && ref_dtype != HR_F32 && ref_dtype != HR_BF16) return fail(HR_EINVAL, "ref_dtype must be HR_F32 or HR_BF16");
     if (rows == 0) {
         if (stats) memset(stats, 0, sizeof *stats);
@@ -650,18 +672,26 @@ int dequant_check(const void* codes, const void* scales, const void* zeros, cons
         ins.push_back({"ref", reinterpret_cast<uintptr_t>(ref),
                        reinterpret_cast<uintptr_t>(ref) + (size_t)(rows * n) * dtype_size(ref_dtype)});
     }
+    std::vector<Range> outs;
     if (deq) {
         if ((st = check_ptr(deq, "deq", 16))) return st;
-        Range rd{"deq", reinterpret_cast<uintptr_t>(deq), reinterpret_cast<uintptr_t>(deq) + (size_t)(rows * n) * 4};
-        for (const Range& r : ins)
-            if (r.hi > r.lo && overlap(r, rd)) return fail(HR_EINVAL, "deq overlaps %s", r.name);
+        outs.push_back({"deq", reinterpret_cast<uintptr_t>(deq), reinterpret_cast<uintptr_t>(deq) + (size_t)(rows * n) * 4});
     }
+    if (stats) {
+        if ((st = check_ptr(work, "work", 16))) return st;
+        outs.push_back({"work", reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + HR_DQ_WORK_BYTES});
+    }
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (r.hi > r.lo && overlap(r, o)) return fail(HR_EINVAL, "%s overlaps %s", o.name, r.name);
+    if ((st = check_disjoint(outs))) return st;
     hr::DqArgs a{};
     a.codes = static_cast<const uint8_t*>(codes);
     a.scales = scales;
     a.zeros = static_cast<const uint8_t*>(zeros);
     a.ref = stats ? ref : nullptr;
     a.deq = deq;
+    a.parts = stats ? work : nullptr;
     a.total = rows * n;
     a.format = qs.format;
     a.sym = qs.sym;
@@ -669,36 +699,37 @@ int dequant_check(const void* codes, const void* scales, const void* zeros, cons
     a.scale_dtype = qs.scale_dtype;
     a.tscale = qs.tscale;
     a.ref_bf16 = ref_dtype == HR_BF16;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hr::DqAccum* acc = nullptr;
-    if (stats) {
-        hipError_t e = hipMalloc(reinterpret_cast<void**>(&acc), sizeof(hr::DqAccum));
-        if (e != hipSuccess) return fail(HR_EDEVICE, "hipMalloc failed: %s", hipGetErrorString(e));
-        e = hipMemsetAsync(acc, 0, sizeof(hr::DqAccum), s);
-        if (e != hipSuccess) {
-            (void)hipFree(acc);
-            return fail(HR_EDEVICE, "hipMemsetAsync failed: %s", hipGetErrorString(e));
-        }
-        a.stats = acc;
-    }
     const int le = hr::launch_dequant(a, stream);
-    if (le != 0) {
-        if (acc) (void)hipFree(acc);
-        return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(le)));
-    }
+    if (le != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(le)));
     if (stats) {
-        hr::DqAccum h;
-        hipError_t e = hipMemcpyAsync(&h, acc, sizeof h, hipMemcpyDeviceToHost, s);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hr::DqPartial h;
+        hipError_t e = hipMemcpyAsync(&h, static_cast<const hr::DqPartial*>(work) + hr::kDqMaxParts, sizeof h,
+                                      hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
-        (void)hipFree(acc);
         if (e != hipSuccess) return fail(HR_EDEVICE, "reading statistics failed: %s", hipGetErrorString(e));
-        float mx;
-        memcpy(&mx, &h.max_err_bits, sizeof mx);
-        stats->max_err_steps = mx;
+        stats->max_err_steps = h.max_err;
         stats->n_over_half_step = static_cast<int64_t>(h.n_over);
         stats->n_clamped = static_cast<int64_t>(h.n_clamped);
         stats->rel_l2_err = h.sum_ref2 > 0 ? sqrt(h.sum_err2 / h.sum_ref2) : 0.0;
     }
+    return ok();
+}
+
+void hr_set_generic_only(int on) { g_generic_only.store(on ? 1 : 0, std::memory_order_relaxed); }
+
+int hr_check_shape(int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q, int nq) {
+    int st = check_shape(dtype, rows, n);
+    if (st) return st;
+    Geometry geo;
+    if ((st = check_block(n, block, &geo))) return st;
+    if (nq < 0 || nq > hr::kMaxQuant) return fail(HR_EINVAL, "nq = %d must be 0, 1 or 2", nq);
+    if (nq > 0 && !q) return fail(HR_EINVAL, "q must be given when nq > 0");
+    QSpec qs[hr::kMaxQuant];
+    for (int i = 0; i < nq; ++i)
+        if ((st = check_qspec(&q[i], n, &qs[i]))) return st;
+    hr::RotPlan p;
+    if ((st = make_plan(dtype, rows > 0 ? rows : 1, n, geo, qs, nq, &p))) return st;
     return ok();
 }
 

@@ -551,16 +551,20 @@ __device__ __forceinline__ float e2m1_mag(uint32_t idx) {
     return t[idx & 7u];
 }
 
+// Dequantizes (and, with a.parts, measures against a.ref) the code bytes of
+// a grid-stride range; each workgroup writes one partial of its statistics.
 __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // byte index
     double se2 = 0.0, sr2 = 0.0;
     unsigned long long nover = 0, nclamp = 0;
     float mx = 0.0f;
-    if (2 * i < a.total) {
+    const int64_t bytes = (a.total + 1) / 2;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < bytes;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const uint32_t byte = a.codes[i];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t e = 2 * i + h;
+            if (e >= a.total) break;
             const uint32_t c = (byte >> (4 * h)) & 0xFu;
             const int64_t G = e >> a.logg;
             float deq, step, lo_lim = 0.0f, hi_lim = 0.0f, s = 1.0f, z = 0.0f;
@@ -593,7 +597,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
                 step = s;
             }
             if (a.deq) a.deq[e] = deq;
-            if (a.stats) {
+            if (a.parts) {
                 const float r = a.ref_bf16 ? bf2f(static_cast<const uint16_t*>(a.ref)[e])
                                            : static_cast<const float*>(a.ref)[e];
                 bool clamped;
@@ -623,8 +627,8 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
             }
         }
     }
-    if (a.stats) {
-        // wave reduction, then one atomic per wave
+    if (a.parts) {
+        // wave reduction, then the four waves in order: one partial per workgroup
         for (int m = 32; m >= 1; m >>= 1) {
             se2 += __shfl_xor(se2, m);
             sr2 += __shfl_xor(sr2, m);
@@ -632,15 +636,45 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DqArgs a) {
             nclamp += __shfl_xor(nclamp, m);
             mx = fmaxf(mx, __shfl_xor(mx, m));
         }
-        if ((threadIdx.x & 63) == 0) {
-            DqAccum* acc = static_cast<DqAccum*>(a.stats);
-            atomicAdd(&acc->sum_err2, se2);
-            atomicAdd(&acc->sum_ref2, sr2);
-            atomicAdd(&acc->n_over, nover);
-            atomicAdd(&acc->n_clamped, nclamp);
-            atomicMax(&acc->max_err_bits, __float_as_uint(mx));
+        __shared__ DqPartial wsum[4];
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) wsum[w] = DqPartial{se2, sr2, nover, nclamp, mx, 0u};
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            DqPartial t = wsum[0];
+            for (int k = 1; k < 4; ++k) {
+                t.sum_err2 += wsum[k].sum_err2;
+                t.sum_ref2 += wsum[k].sum_ref2;
+                t.n_over += wsum[k].n_over;
+                t.n_clamped += wsum[k].n_clamped;
+                t.max_err = fmaxf(t.max_err, wsum[k].max_err);
+            }
+            static_cast<DqPartial*>(a.parts)[blockIdx.x] = t;
         }
     }
+}
+
+// Sums the `nparts` partials of dequant_kernel in a fixed order into slot
+// kDqMaxParts (one workgroup of 64 threads).
+__global__ void __launch_bounds__(64) dequant_finish(DqPartial* parts, int nparts) {
+    const int t = threadIdx.x;
+    DqPartial acc{0.0, 0.0, 0ull, 0ull, 0.0f, 0u};
+    for (int i = t; i < nparts; i += 64) {
+        const DqPartial p = parts[i];
+        acc.sum_err2 += p.sum_err2;
+        acc.sum_ref2 += p.sum_ref2;
+        acc.n_over += p.n_over;
+        acc.n_clamped += p.n_clamped;
+        acc.max_err = fmaxf(acc.max_err, p.max_err);
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+        acc.sum_err2 += __shfl_xor(acc.sum_err2, m);
+        acc.sum_ref2 += __shfl_xor(acc.sum_ref2, m);
+        acc.n_over += __shfl_xor(acc.n_over, m);
+        acc.n_clamped += __shfl_xor(acc.n_clamped, m);
+        acc.max_err = fmaxf(acc.max_err, __shfl_xor(acc.max_err, m));
+    }
+    if (t == 0) parts[kDqMaxParts] = acc;
 }
 
 template <int LOGE, bool BF16, int KMAX>
@@ -692,8 +726,13 @@ int launch_rotate(const RotPlan& p, void* stream) {
 int launch_dequant(const DqArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t bytes = (a.total + 1) / 2;
-    const int64_t grid = (bytes + 255) / 256;
+    int64_t grid = (bytes + 255) / 256;
+    if (grid > kDqMaxParts) grid = kDqMaxParts;   // grid-stride beyond that
     hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.parts) return static_cast<int>(e);
+    hipLaunchKernelGGL(dequant_finish, dim3(1), dim3(64), 0, s, static_cast<DqPartial*>(a.parts),
+                       static_cast<int>(grid));
     return static_cast<int>(hipGetLastError());
 }
 

@@ -13,6 +13,7 @@
 // smallest K = odd(n) * 2^j (j >= 0) dividing n with such a construction.
 #include <stdint.h>
 
+#include <cstddef>
 #include <vector>
 
 namespace hr {

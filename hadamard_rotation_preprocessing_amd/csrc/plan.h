@@ -68,21 +68,25 @@ struct DqArgs {
     const uint8_t* zeros;
     const void* ref;       // nullable
     float* deq;            // nullable
-    void* stats;           // nullable: DqAccum on the device
+    void* parts;           // nullable: DqPartial[kDqMaxParts + 1] on the device (statistics)
     int64_t total;         // elements
     int32_t format, sym, logg, scale_dtype, ref_bf16;
     float tscale;          // NVFP4 tensor scale
 };
 
-// Device accumulators of dequant_check.
-struct DqAccum {
+// Statistics of dequant_check: one partial per workgroup of a grid of at
+// most kDqMaxParts workgroups, then their sum (in a fixed order, so the
+// result does not depend on scheduling) in slot kDqMaxParts.
+struct DqPartial {
     double sum_err2;
     double sum_ref2;
     unsigned long long n_over;
     unsigned long long n_clamped;
-    unsigned int max_err_bits;   // non-negative float as bits (monotone)
-    unsigned int pad;
+    float max_err;
+    uint32_t pad;
 };
+constexpr int kDqMaxParts = 1024;
+constexpr size_t kDqWorkBytes = sizeof(DqPartial) * (kDqMaxParts + 1);
 
 // Arguments of the specialised bfloat16 kernels (one wave per block).
 struct FastArgs {

@@ -51,9 +51,12 @@
  *     flattened group index, ceil(groups / 2) bytes, a trailing odd nibble
  *     set to 0.
  *   - Ownership: the caller allocates every buffer on the device of the
- *     stream and keeps it alive until the stream work has completed.  The
- *     library keeps no pointer after returning and allocates no device
- *     memory, except dequant_check with non-NULL `stats` (see there).
+ *     stream, including dequant_check's statistics workspace, and keeps it
+ *     alive until the stream work has completed.  The library keeps no
+ *     pointer after returning and allocates no device memory.  Its only
+ *     mutable state is the per-thread error text, per-device launch sizes
+ *     cached on first use, and the process-wide dispatch switch of
+ *     hr_set_generic_only.
  *   - Alignment: x, y, y_rot, w, w_rot and codes must be 16-byte aligned;
  *     scales and zeros naturally aligned.  Outputs may not overlap inputs or
  *     each other, except y == x (hadamard_rotate) and y_rot == x
@@ -66,7 +69,8 @@
  *     returns the message of the last failing call on this thread.
  *   - rows == 0 is a valid empty tensor: the call returns HR_OK and enqueues
  *     nothing (pointers may then be NULL).
- *   - Graph capture: apart from dequant_check with `stats`, a call enqueues
+ *   - Graph capture: apart from dequant_check with `stats` (which copies
+ *     to the host and synchronises), a call enqueues
  *     kernel launches only (no allocation, copy or memset), so it may be
  *     captured in a HIP graph and replayed.  The first call for a kernel on a
  *     device also queries the device's occupancy on the host; making one call
@@ -210,18 +214,24 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
  *   codes, scales, zeros  as written by the calls above for [rows, n].
  *   ref    device or NULL: [rows, n] of ref_dtype (HR_F32 / HR_BF16).
  *   deq    device or NULL: [rows, n] float32 output.
- *   stats  host or NULL: requires ref.  Filled after the stream has been
- *          synchronised (this call then blocks).  The local step is s for
- *          INT; for MXFP4 it is 2^e times the E2M1 spacing around |ref| / 2^e
- *          (0.5 below 2, 1 below 4, 2 above).  Clamped: INT ref/s (+ z)
- *          outside [qmin - 1/2, qmax + 1/2]; MXFP4 |ref| / 2^e > 6.  With
- *          stats, the call allocates and frees a few bytes of device memory
- *          for the reduction.
+ *   stats  host or NULL: requires ref and work.  Filled after the stream
+ *          has been synchronised (this call then blocks).  The local step is
+ *          s for INT; for MXFP4 it is 2^e times the E2M1 spacing around
+ *          |ref| / 2^e (0.5 below 2, 1 below 4, 2 above).  Clamped: INT
+ *          ref/s (+ z) outside [qmin - 1/2, qmax + 1/2]; MXFP4 |ref| / 2^e > 6.
+ *          The sums are reduced in a fixed order (per-workgroup partials,
+ *          then one pass over them), so repeated calls give identical stats.
+ *   work   device or NULL: HR_DQ_WORK_BYTES of scratch for the statistics
+ *          reduction, 16-byte aligned, owned by the caller; required with
+ *          stats, ignored without.  Its contents on entry do not matter;
+ *          it may not overlap any other buffer of the call.
  * At least one of deq and stats must be given.
  */
+#define HR_DQ_WORK_BYTES 65536
 int dequant_check(const void* codes, const void* scales, const void* zeros,
                   const hr_qspec* q, int64_t rows, int64_t n, const void* ref,
-                  int ref_dtype, float* deq, hr_dq_stats* stats, void* stream);
+                  int ref_dtype, float* deq, hr_dq_stats* stats, void* work,
+                  void* stream);
 
 /*
  * Randomised rotations: the rotation becomes R' = P . D_in . R . D_out with
@@ -273,6 +283,27 @@ const char* hr_last_error(void);
  * base matrix entries (+1 / -1, row-major int8) the library applies.
  */
 int hr_kron_order(int64_t n, int32_t* K, int64_t* M, int8_t* hk);
+
+/*
+ * Host-only query: the status that hadamard_rotate (nq = 0),
+ * rotate_quantize_act (nq = 1) or rotate_fuse_weight (nq = 0..2) would
+ * return for this dtype, shape, block and quantizer specs q[0..nq), from the
+ * same argument checks and launch planning, before any pointer is looked at.
+ * Touches no device.  rows <= 0 is planned as one row.  Lets a caller learn
+ * whether a shape is implemented (HR_OK) or not (HR_EUNSUPPORTED, with the
+ * reason in hr_last_error) before allocating anything.
+ */
+int hr_check_shape(int dtype, int64_t rows, int64_t n, int64_t block, const hr_qspec* q, int nq);
+
+/*
+ * Dispatch switch for testing: on != 0 sends every later call in the
+ * process to the generic kernel, which handles every supported shape, even
+ * where a specialised kernel matches; 0 (the default) restores the normal
+ * dispatch.  Results agree within the tolerances of the library's tests,
+ * not bit for bit.  Process-wide; not synchronised with calls in flight on
+ * other threads.
+ */
+void hr_set_generic_only(int on);
 
 #ifdef __cplusplus
 }

@@ -129,13 +129,62 @@ def test_dequant_check_validation():
     lib = L.lib()
     st = L.hr_dq_stats()
     spec = q(sym=1)
-    assert lib.dequant_check(B, C, None, spec, 4, 4096, None, L.HR_F32, None, None, None) == L.HR_EINVAL
+    W = ctypes.c_void_p(P + 7 * (1 << 36))
+    f = lib.dequant_check
+    assert f(B, C, None, spec, 4, 4096, None, L.HR_F32, None, None, None, None) == L.HR_EINVAL
     assert "nothing to compute" in msg()
-    assert lib.dequant_check(B, C, None, spec, 4, 4096, None, L.HR_F32, None, ctypes.byref(st), None) == L.HR_EINVAL
+    assert f(B, C, None, spec, 4, 4096, None, L.HR_F32, None, ctypes.byref(st), W, None) == L.HR_EINVAL
     assert "requires ref" in msg()
-    assert lib.dequant_check(B, C, None, spec, 4, 4096, A, 9, None, ctypes.byref(st), None) == L.HR_EINVAL
-    assert lib.dequant_check(B, C, None, spec, 4, 4096, A, L.HR_F32, ctypes.c_void_p(P + 64), None, None) == L.HR_EINVAL
+    assert f(B, C, None, spec, 4, 4096, A, L.HR_F32, None, ctypes.byref(st), None, None) == L.HR_EINVAL
+    assert "requires work" in msg()
+    assert f(B, C, None, spec, 4, 4096, A, 9, None, ctypes.byref(st), W, None) == L.HR_EINVAL
+    assert f(B, C, None, spec, 4, 4096, A, L.HR_F32, ctypes.c_void_p(P + 64), None, None, None) == L.HR_EINVAL
     assert "deq overlaps" in msg()
+    # the workspace is written: it may not overlap an input or deq
+    assert f(B, C, None, spec, 4, 4096, A, L.HR_F32, None, ctypes.byref(st), ctypes.c_void_p(P + 4096),
+             None) == L.HR_EINVAL
+    assert "work overlaps" in msg()
+    assert f(B, C, None, spec, 4, 4096, A, L.HR_F32, D, ctypes.byref(st), ctypes.c_void_p(D.value + 256),
+             None) == L.HR_EINVAL
+    assert "overlap" in msg()
+    assert f(B, C, None, spec, 4, 4096, A, L.HR_F32, None, ctypes.byref(st), ctypes.c_void_p(W.value + 8),
+             None) == L.HR_EINVAL
+    assert "aligned" in msg()
+    # empty: stats zeroed without touching the device
+    st.n_clamped = 5
+    assert f(None, None, None, spec, 0, 4096, A, L.HR_F32, None, ctypes.byref(st), W, None) == L.HR_OK
+    assert st.n_clamped == 0
+
+
+def cs(dt=L.HR_BF16, rows=4, n=4096, block=0, specs=(), nq=None):
+    arr = (L.hr_qspec * max(1, len(specs)))(*specs)
+    return L.lib().hr_check_shape(dt, rows, n, block, arr, len(specs) if nq is None else nq)
+
+
+def spec_int(g, sym):
+    return L.hr_qspec(L.HR_Q_INT, 4, g, 1 if sym else 0, L.HR_BF16, 0.0)
+
+
+@pytest.mark.parametrize("n,block,g", [(16384, 0, 16384), (14336, 0, 2048), (12288, 0, 4096), (16384, 0, 8192),
+                                       (32768, 16384, 16384), (4096, 0, 4096)])
+def test_wide_asymmetric_groups_are_planned(n, block, g):
+    """Asymmetric groups so wide that a chunk holds an odd number of them
+    (chunks are then paired so that zero-point bytes are whole): planned with
+    at most 1024 threads per workgroup."""
+    assert cs(n=n, block=block, specs=[spec_int(g, False)]) == L.HR_OK, msg()
+
+
+def test_check_shape_refusals():
+    # a single asymmetric group of 32768: a pair of chunks needs 2048 threads
+    assert cs(n=32768, specs=[spec_int(32768, False)]) == L.HR_EUNSUPPORTED
+    assert "threads" in msg()
+    assert cs(n=32768, specs=[spec_int(32768, True)]) == L.HR_OK
+    assert cs(n=128 * 108, specs=[spec_int(128, True)]) == L.HR_EUNSUPPORTED
+    assert cs(n=4096, block=3) == L.HR_EINVAL
+    assert cs(n=4096, specs=[spec_int(128, True)], nq=3) == L.HR_EINVAL
+    assert cs(dt=7) == L.HR_EINVAL
+    assert cs(n=4096, specs=[spec_int(128, True), L.hr_qspec(L.HR_Q_MXFP4, 4, 32, 1, L.HR_E8M0, 0.0)]) == L.HR_OK
+    assert cs(rows=0, n=4096) == L.HR_OK
 
 
 @pytest.mark.parametrize("n", [14336, 96, 5120, 12, 20 * 32, 60 * 8])
@@ -201,3 +250,27 @@ def test_weight_out_validation():
     assert "overlaps" in msg()
     assert f(NUL, L.HR_BF16, 4096, 4096, 0, B, None) == L.HR_EINVAL
     assert f(NUL, L.HR_BF16, 0, 4096, 0, NUL, None) == L.HR_OK
+
+
+def test_planning_sweep():
+    """Plan a broad set of shapes, blocks and quantizer specs through
+    hr_check_shape (under the sanitizer build this exercises the planner's
+    arithmetic everywhere); every status is one of the documented ones and
+    every refusal carries a message."""
+    widths = [2 ** k for k in range(1, 16)] + [12 * 512, 20 * 256, 28 * 512, 60 * 512, 12 * 1024, 96, 100, 108 * 128]
+    specs = [spec_int(g, s) for g in (2, 4, 8, 16, 32, 64, 128, 256, 2048, 32768) for s in (True, False)]
+    specs += [L.hr_qspec(L.HR_Q_MXFP4, 4, 32, 1, L.HR_E8M0, 0.0), L.hr_qspec(L.HR_Q_NVFP4, 4, 16, 1, L.HR_E4M3, 0.5)]
+    seen = set()
+    for n in widths:
+        for block in (0, 16, 32, 128, 2048, n):
+            for dt in (L.HR_BF16, L.HR_F32):
+                st = cs(dt=dt, rows=3, n=n, block=block)
+                assert st in (L.HR_OK, L.HR_EINVAL, L.HR_EUNSUPPORTED)
+                for sp in specs:
+                    st = cs(dt=dt, rows=5, n=n, block=block, specs=[sp])
+                    assert st in (L.HR_OK, L.HR_EINVAL, L.HR_EUNSUPPORTED)
+                    assert (st == L.HR_OK) == (msg() == ""), (n, block, st, msg())
+                    seen.add(st)
+                st = cs(dt=dt, rows=7, n=n, block=block, specs=[specs[-2], specs[13]])
+                assert st in (L.HR_OK, L.HR_EINVAL, L.HR_EUNSUPPORTED)
+    assert seen == {L.HR_OK, L.HR_EINVAL, L.HR_EUNSUPPORTED}

@@ -32,14 +32,12 @@ def gpu_ready():
 
 
 @pytest.fixture(params=["fast", "generic"])
-def kernel_path(request, monkeypatch):
+def kernel_path(request):
     """Run a test through the specialised bf16 kernels (default dispatch) and
-    again with the generic kernel forced."""
-    if request.param == "generic":
-        monkeypatch.setenv("HADAROT_FORCE_GENERIC", "1")
-    else:
-        monkeypatch.delenv("HADAROT_FORCE_GENERIC", raising=False)
-    return request.param
+    again with the generic kernel forced (hr_set_generic_only)."""
+    hr.set_generic_only(request.param == "generic")
+    yield request.param
+    hr.set_generic_only(False)
 
 
 def dtname(t):
@@ -177,19 +175,38 @@ def test_maximum_widths(case):
     run_act(x, n, block, spec, y_rot=True)
 
 
-@pytest.mark.parametrize("case", [(32768, 0, hr.QSpec.nvfp4(0.5)), (16384, 16384, hr.QSpec("int", 4, 8, True, "bf16")),
-                                  (8192, 8192, hr.QSpec("int", 4, 4, False, "f32")),
-                                  (32768, 32768, hr.QSpec("int", 4, 2, False, "bf16")),
-                                  (4096, 4096, hr.QSpec("int", 4, 2, True, "f32"))],
-                         ids=["full-32768-nvfp4", "b16384-int-g8", "b8192-asym-g4", "b32768-asym-g2", "b4096-g2"])
+@pytest.mark.parametrize("case", [(32768, 0, hr.QSpec.nvfp4(0.5), "bf16"),
+                                  (16384, 16384, hr.QSpec("int", 4, 8, True, "bf16"), "bf16"),
+                                  (8192, 8192, hr.QSpec("int", 4, 4, False, "f32"), "bf16"),
+                                  (32768, 32768, hr.QSpec("int", 4, 2, False, "bf16"), "bf16"),
+                                  (4096, 4096, hr.QSpec("int", 4, 2, True, "f32"), "bf16"),
+                                  (32768, 0, hr.QSpec("int", 4, 4, False, "f32"), "f32"),
+                                  (30720, 0, hr.QSpec.nvfp4(), "bf16"),
+                                  (30720, 0, hr.QSpec("int", 4, 8, True, "bf16"), "bf16"),
+                                  (30720, 0, hr.QSpec("int", 4, 8, False, "f32"), "f32")],
+                         ids=["full-32768-nvfp4", "b16384-int-g8", "b8192-asym-g4", "b32768-asym-g2", "b4096-g2",
+                              "f32-full-32768-asym-g4", "kron60x512-nvfp4", "kron60x512-int-g8",
+                              "f32-kron60x512-asym-g8"])
 def test_more_than_1024_groups_per_block(case):
     """Blocks of more than 1024 groups: each thread of the generic kernel
     quantizes several whole groups (asymmetric zero points written per
-    thread)."""
-    n, block, spec = case
-    x = synth.gaussian((3, n), seed=5200 + n + spec.group_size, dtype=torch.bfloat16)
+    thread), on bfloat16 and float32 inputs and after the Kronecker mix."""
+    n, block, spec, dt = case
+    x = synth.gaussian((3, n), seed=5200 + n + spec.group_size, dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
     x[1, : n // 3] = 0.0
     run_act(x, n, block, spec, y_rot=True)
+
+
+@pytest.mark.parametrize("case", [(16384, 0, 16384), (14336, 0, 2048), (12288, 0, 4096), (16384, 0, 8192)],
+                         ids=["full-16384-one-group", "kron28x512-g2048", "kron12x1024-g4096", "full-16384-g8192"])
+def test_wide_asymmetric_groups(case):
+    """Asymmetric groups of 2048..16384 (an odd number of groups per chunk):
+    the chunks are taken in pairs so that zero-point bytes are whole, with 32
+    elements per thread where a pair would need more than 1024 threads."""
+    n, block, g = case
+    x = synth.gaussian((5, n), seed=5300 + n + g, dtype=torch.bfloat16)
+    x[2] *= 1e-3
+    run_act(x, n, block, hr.QSpec("int", 4, g, False, "bf16"), y_rot=True)
 
 
 def test_weight_fusion_two_group_sizes_wide():
