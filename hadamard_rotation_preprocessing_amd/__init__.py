@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     rotate_quantize_act(x, block, qspec, y_rot=False)  -> rotate_quantize_act
     rotate_fuse_weight(w, block, qspecs, w_rot=True)   -> rotate_fuse_weight
     dequant_check(q, qspec, ref=None, ...)             -> dequant_check
+    dequant_check_noalloc(q, qspec, ref=None, ...)     -> dequant_check_noalloc
     rotate_fuse_weight_out(w, block=0, out=None)       -> rotate_fuse_weight_out
 With ``mix=dict(perm=..., in_signs=..., out_signs=...)`` (device tensors,
 int32 / int8 / int8, any subset) the first three call the ``*_mixed`` entry
@@ -27,6 +28,7 @@ from . import _lib as L
 from ._lib import HadarotError, check, lib  # noqa: F401
 
 __all__ = ["QSpec", "rotate", "rotate_quantize_act", "rotate_fuse_weight", "rotate_fuse_weight_out", "dequant_check",
+           "dequant_check_noalloc",
            "hadamard_rotate", "kron_order", "check_shape", "set_generic_only", "HadarotError", "alloc_quant_outputs"]
 
 _SCALE_CODES = {"f32": L.HR_F32, "bf16": L.HR_BF16, "e8m0": L.HR_E8M0, "e4m3": L.HR_E4M3}
@@ -192,24 +194,48 @@ def rotate_fuse_weight_out(w: torch.Tensor, block: int = 0, out: torch.Tensor | 
 
 
 def dequant_check(q: dict, qspec: QSpec, rows: int, n: int, ref: torch.Tensor | None = None,
-                  want_deq: bool = True, want_stats: bool = True):
+                  want_deq: bool = True, want_stats: bool = True, deq: torch.Tensor | None = None,
+                  work: torch.Tensor | None = None):
     """Dequantize packed outputs; returns (deq float32 [rows, n] or None,
-    stats dict or None).  Stats need ``ref`` and synchronise the stream."""
+    stats dict or None).  Stats need ``ref`` and synchronise the stream; their
+    workspace (``work``, HR_DQ_WORK_BYTES bytes) is allocated with torch when
+    not given."""
     codes = q["codes"]
     dev = codes.device
-    deq = torch.empty((rows, n), dtype=torch.float32, device=dev) if want_deq else None
+    if want_deq and deq is None:
+        deq = torch.empty((rows, n), dtype=torch.float32, device=dev)
+    if not want_deq:
+        deq = None
     st = L.hr_dq_stats()
     spec = qspec.c()
     ref_dt = _dt(ref) if ref is not None else L.HR_F32
-    work = torch.empty(L.HR_DQ_WORK_BYTES, dtype=torch.uint8, device=dev) if want_stats else None
+    if want_stats and work is None:
+        work = torch.empty(L.HR_DQ_WORK_BYTES, dtype=torch.uint8, device=dev)
     check(lib().dequant_check(_ptr(codes), _ptr(q["scales"]), _ptr(q.get("zeros")),
                               ctypes.byref(spec), rows, n, _ptr(ref), ref_dt, _ptr(deq),
-                              ctypes.byref(st) if want_stats else None, _ptr(work), _stream(codes)))
-    stats = None
-    if want_stats:
-        stats = dict(max_err_steps=st.max_err_steps, n_over_half_step=st.n_over_half_step,
-                     n_clamped=st.n_clamped, rel_l2_err=st.rel_l2_err)
-    return deq, stats
+                              ctypes.byref(st) if want_stats else None, _ptr(work) if want_stats else None,
+                              _stream(codes)))
+    return deq, (_stats(st) if want_stats else None)
+
+
+def dequant_check_noalloc(q: dict, qspec: QSpec, rows: int, n: int, ref: torch.Tensor | None = None,
+                          deq: torch.Tensor | None = None, want_stats: bool = True):
+    """dequant_check with the library's static device scratch instead of a
+    workspace: the C call allocates nothing (``deq``, if wanted, is the
+    caller's float32 [rows, n] tensor).  Returns (deq, stats or None)."""
+    codes = q["codes"]
+    st = L.hr_dq_stats()
+    spec = qspec.c()
+    ref_dt = _dt(ref) if ref is not None else L.HR_F32
+    check(lib().dequant_check_noalloc(_ptr(codes), _ptr(q["scales"]), _ptr(q.get("zeros")),
+                                      ctypes.byref(spec), rows, n, _ptr(ref), ref_dt, _ptr(deq),
+                                      ctypes.byref(st) if want_stats else None, _stream(codes)))
+    return deq, (_stats(st) if want_stats else None)
+
+
+def _stats(st) -> dict:
+    return dict(max_err_steps=st.max_err_steps, n_over_half_step=st.n_over_half_step,
+                n_clamped=st.n_clamped, rel_l2_err=st.rel_l2_err)
 
 
 def check_shape(dtype: torch.dtype, rows: int, n: int, block: int, qspecs=()) -> None:

@@ -21,7 +21,7 @@ HR_Q_INT, HR_Q_MXFP4, HR_Q_NVFP4 = 0, 1, 2
 EXPORTS = ("hadamard_rotate", "rotate_quantize_act", "rotate_fuse_weight",
            "dequant_check", "hr_last_error", "hr_kron_order",
            "hadamard_rotate_mixed", "rotate_quantize_act_mixed", "rotate_fuse_weight_mixed",
-           "rotate_fuse_weight_out", "hr_check_shape", "hr_set_generic_only")
+           "rotate_fuse_weight_out", "hr_check_shape", "hr_set_generic_only", "dequant_check_noalloc")
 HR_DQ_WORK_BYTES = 65536
 
 
@@ -76,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.dequant_check.argtypes = [vp, vp, vp, ctypes.POINTER(hr_qspec), i64, i64, vp, ci, vp,
                                     ctypes.POINTER(hr_dq_stats), vp, vp]
         L.dequant_check.restype = ci
+        L.dequant_check_noalloc.argtypes = [vp, vp, vp, ctypes.POINTER(hr_qspec), i64, i64, vp, ci, vp,
+                                            ctypes.POINTER(hr_dq_stats), vp]
+        L.dequant_check_noalloc.restype = ci
         L.hr_last_error.argtypes = []
         L.hr_last_error.restype = ctypes.c_char_p
         L.hr_kron_order.argtypes = [i64, ctypes.POINTER(i32), ctypes.POINTER(i64), vp]

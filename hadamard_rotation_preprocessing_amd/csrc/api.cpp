@@ -548,6 +548,88 @@ int weight_impl(const void* w, int dtype, int64_t out_features, int64_t in_featu
     return run(p, stream);
 }
 
+// dequant_check and dequant_check_noalloc: the statistics partials go to
+// the caller's `work` or, with use_static, to the library's static device
+// scratch (no allocation either way).
+int dequant_impl(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
+                 int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* work,
+                 bool use_static, void* stream) {
+    static_assert(hr::kDqWorkBytes <= HR_DQ_WORK_BYTES, "dequant_check workspace");
+    int st = check_shape(HR_F32, rows, n);
+    if (st) return st;
+    QSpec qs;
+    if ((st = check_qspec(q, n, &qs))) return st;
+    if (!deq && !stats) return fail(HR_EINVAL, "nothing to compute: deq and stats are NULL");
+    if (stats && !ref) return fail(HR_EINVAL, "stats requires ref");
+    if (stats && !work && !use_static)
+        return fail(HR_EINVAL, "stats requires work (HR_DQ_WORK_BYTES of device memory)");
+    if (ref && ref_dtype != HR_F32 && ref_dtype != HR_BF16) return fail(HR_EINVAL, "ref_dtype must be HR_F32 or HR_BF16");
+    if (rows == 0) {
+        if (stats) memset(stats, 0, sizeof *stats);
+        return ok();
+    }
+    QBuf b;
+    if ((st = check_qbuffers(qs, rows, n, const_cast<void*>(codes), const_cast<void*>(scales),
+                             const_cast<void*>(zeros), "", &b)))
+        return st;
+    std::vector<Range> ins{b.codes, b.scales, b.zeros};
+    if (ref) {
+        if ((st = check_ptr(ref, "ref", 16))) return st;
+        ins.push_back({"ref", reinterpret_cast<uintptr_t>(ref),
+                       reinterpret_cast<uintptr_t>(ref) + (size_t)(rows * n) * dtype_size(ref_dtype)});
+    }
+    std::vector<Range> outs;
+    if (deq) {
+        if ((st = check_ptr(deq, "deq", 16))) return st;
+        outs.push_back({"deq", reinterpret_cast<uintptr_t>(deq), reinterpret_cast<uintptr_t>(deq) + (size_t)(rows * n) * 4});
+    }
+    if (stats && !use_static) {
+        if ((st = check_ptr(work, "work", 16))) return st;
+        outs.push_back({"work", reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + HR_DQ_WORK_BYTES});
+    }
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (r.hi > r.lo && overlap(r, o)) return fail(HR_EINVAL, "%s overlaps %s", o.name, r.name);
+    if ((st = check_disjoint(outs))) return st;
+    if (stats && use_static) {
+        // one call's partials: at most kDqMaxParts + 1 slots whatever the
+        // input size (the grid is capped and strides over the rest), which
+        // the static scratch holds (checked at compile time)
+        const int e = hr::scratch_address(&work);
+        if (e != 0)
+            return fail(HR_EDEVICE, "static scratch unavailable: %s", hipGetErrorString(static_cast<hipError_t>(e)));
+    }
+    hr::DqArgs a{};
+    a.codes = static_cast<const uint8_t*>(codes);
+    a.scales = scales;
+    a.zeros = static_cast<const uint8_t*>(zeros);
+    a.ref = stats ? ref : nullptr;
+    a.deq = deq;
+    a.parts = stats ? work : nullptr;
+    a.total = rows * n;
+    a.format = qs.format;
+    a.sym = qs.sym;
+    a.logg = qs.logg;
+    a.scale_dtype = qs.scale_dtype;
+    a.tscale = qs.tscale;
+    a.ref_bf16 = ref_dtype == HR_BF16;
+    const int le = hr::launch_dequant(a, stream);
+    if (le != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(le)));
+    if (stats) {
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hr::DqPartial h;
+        hipError_t e = hipMemcpyAsync(&h, static_cast<const hr::DqPartial*>(work) + hr::kDqMaxParts, sizeof h,
+                                      hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return fail(HR_EDEVICE, "reading statistics failed: %s", hipGetErrorString(e));
+        stats->max_err_steps = h.max_err;
+        stats->n_over_half_step = static_cast<int64_t>(h.n_over);
+        stats->n_clamped = static_cast<int64_t>(h.n_clamped);
+        stats->rel_l2_err = h.sum_ref2 > 0 ? sqrt(h.sum_err2 / h.sum_ref2) : 0.0;
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -649,71 +731,12 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
 int dequant_check(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
                   int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* work,
                   void* stream) {
-    static_assert(hr::kDqWorkBytes <= HR_DQ_WORK_BYTES, "dequant_check workspace");
-    int st = check_shape(HR_F32, rows, n);
-    if (st) return st;
-    QSpec qs;
-    if ((st = check_qspec(q, n, &qs))) return st;
-    if (!deq && !stats) return fail(HR_EINVAL, "nothing to compute: deq and stats are NULL");
-    if (stats && !ref) return fail(HR_EINVAL, "stats requires ref");
-    if (stats && !work) return fail(HR_EINVAL, "stats requires work (HR_DQ_WORK_BYTES of device memory)");
-    if (ref && ref_dtype != HR_F32 && ref_dtype != HR_BF16) return fail(HR_EINVAL, "ref_dtype must be HR_F32 or HR_BF16");
-    if (rows == 0) {
-        if (stats) memset(stats, 0, sizeof *stats);
-        return ok();
-    }
-    QBuf b;
-    if ((st = check_qbuffers(qs, rows, n, const_cast<void*>(codes), const_cast<void*>(scales),
-                             const_cast<void*>(zeros), "", &b)))
-        return st;
-    std::vector<Range> ins{b.codes, b.scales, b.zeros};
-    if (ref) {
-        if ((st = check_ptr(ref, "ref", 16))) return st;
-        ins.push_back({"ref", reinterpret_cast<uintptr_t>(ref),
-                       reinterpret_cast<uintptr_t>(ref) + (size_t)(rows * n) * dtype_size(ref_dtype)});
-    }
-    std::vector<Range> outs;
-    if (deq) {
-        if ((st = check_ptr(deq, "deq", 16))) return st;
-        outs.push_back({"deq", reinterpret_cast<uintptr_t>(deq), reinterpret_cast<uintptr_t>(deq) + (size_t)(rows * n) * 4});
-    }
-    if (stats) {
-        if ((st = check_ptr(work, "work", 16))) return st;
-        outs.push_back({"work", reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + HR_DQ_WORK_BYTES});
-    }
-    for (const Range& o : outs)
-        for (const Range& r : ins)
-            if (r.hi > r.lo && overlap(r, o)) return fail(HR_EINVAL, "%s overlaps %s", o.name, r.name);
-    if ((st = check_disjoint(outs))) return st;
-    hr::DqArgs a{};
-    a.codes = static_cast<const uint8_t*>(codes);
-    a.scales = scales;
-    a.zeros = static_cast<const uint8_t*>(zeros);
-    a.ref = stats ? ref : nullptr;
-    a.deq = deq;
-    a.parts = stats ? work : nullptr;
-    a.total = rows * n;
-    a.format = qs.format;
-    a.sym = qs.sym;
-    a.logg = qs.logg;
-    a.scale_dtype = qs.scale_dtype;
-    a.tscale = qs.tscale;
-    a.ref_bf16 = ref_dtype == HR_BF16;
-    const int le = hr::launch_dequant(a, stream);
-    if (le != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(le)));
-    if (stats) {
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        hr::DqPartial h;
-        hipError_t e = hipMemcpyAsync(&h, static_cast<const hr::DqPartial*>(work) + hr::kDqMaxParts, sizeof h,
-                                      hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return fail(HR_EDEVICE, "reading statistics failed: %s", hipGetErrorString(e));
-        stats->max_err_steps = h.max_err;
-        stats->n_over_half_step = static_cast<int64_t>(h.n_over);
-        stats->n_clamped = static_cast<int64_t>(h.n_clamped);
-        stats->rel_l2_err = h.sum_ref2 > 0 ? sqrt(h.sum_err2 / h.sum_ref2) : 0.0;
-    }
-    return ok();
+    return dequant_impl(codes, scales, zeros, q, rows, n, ref, ref_dtype, deq, stats, work, false, stream);
+}
+
+int dequant_check_noalloc(const void* codes, const void* scales, const void* zeros, const hr_qspec* q, int64_t rows,
+                          int64_t n, const void* ref, int ref_dtype, float* deq, hr_dq_stats* stats, void* stream) {
+    return dequant_impl(codes, scales, zeros, q, rows, n, ref, ref_dtype, deq, stats, nullptr, true, stream);
 }
 
 void hr_set_generic_only(int on) { g_generic_only.store(on ? 1 : 0, std::memory_order_relaxed); }

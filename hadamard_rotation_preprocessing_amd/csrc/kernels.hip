@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "codes.h"
 #include "plan.h"
 
@@ -721,6 +723,29 @@ hipError_t launch_e(const RotPlan& p, hipStream_t s) {
 int launch_rotate(const RotPlan& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     return static_cast<int>(p.bf16 ? launch_e<true>(p, s) : launch_e<false>(p, s));
+}
+
+// Scratch of dequant_check_noalloc: the statistics partials, one copy per
+// device, held until the process ends.  In host code `scratch` is only a
+// handle for hipGetSymbolAddress; kernels get the device address from
+// scratch_address().
+static __device__ __align__(256) unsigned char scratch[kDqScratchBytes];
+
+int scratch_address(void** out) {
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // with the device current: each device holds its own copy
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return 0;
 }
 
 int launch_dequant(const DqArgs& a, void* stream) {

@@ -87,6 +87,9 @@ struct DqPartial {
 };
 constexpr int kDqMaxParts = 1024;
 constexpr size_t kDqWorkBytes = sizeof(DqPartial) * (kDqMaxParts + 1);
+// static device scratch of dequant_check_noalloc (holds kDqWorkBytes)
+constexpr size_t kDqScratchBytes = 65536;
+static_assert(kDqWorkBytes <= kDqScratchBytes, "statistics partials fit the static scratch");
 
 // Arguments of the specialised bfloat16 kernels (one wave per block).
 struct FastArgs {
@@ -143,10 +146,13 @@ int launch_colrot(const ColArgs& a, void* stream);        // returns hipError_t
 // Launches a specialised kernel if one matches `k`: returns 1 if launched,
 // 0 if none matches, or a negative hipError_t on a launch error.
 int launch_fast(const FastKey& k, const FastArgs& a, void* stream);
-// Launches the specialised Kronecker kernel if one matches (K <= 32,
-// M = 512, bf16, no quantizer or INT g128 with bf16 scales): 1 launched,
-// 0 no match, negative hipError_t on a launch error.
+// Launches a specialised Kronecker kernel if one matches (bf16; K <= 32 with
+// M = 512, or 32 < K <= 160 with M = 128; no quantizer or INT g128 with bf16
+// scales): 1 launched, 0 no match, negative hipError_t on a launch error.
 int launch_kron(const FastKey& k, const KronArgs& a, void* stream);
 int launch_dequant(const DqArgs& a, void* stream);        // returns hipError_t
+// Device address of the static scratch of the current device (resolved once
+// per device); returns hipError_t.
+int scratch_address(void** out);
 
 }  // namespace hr

@@ -234,6 +234,25 @@ int dequant_check(const void* codes, const void* scales, const void* zeros,
                   void* stream);
 
 /*
+ * dequant_check without the `work` argument, for callers that cannot
+ * allocate device memory (harnesses or serving loops that forbid hipMalloc):
+ * the statistics partials go to a 64 KiB scratch array in the library's
+ * device code, one copy per GPU, resolved on the first call on each device
+ * and held until the process ends.  Nothing is allocated.  The scratch a call
+ * needs does not grow with the input (at most 1025 partials of 40 bytes: the
+ * grid is capped at 1024 workgroups, which stride over any size), so every
+ * size dequant_check accepts fits; there is no size limit beyond its own.
+ * Every call writes each scratch slot it reads, so nothing needs clearing
+ * between calls.  Calls with `stats` on one GPU share that scratch: two such
+ * calls in flight at once (other streams or other host threads) race, and
+ * the caller must order them.  Without `stats` the call is dequant_check's
+ * and touches no scratch.  Results equal dequant_check's bit for bit.
+ */
+int dequant_check_noalloc(const void* codes, const void* scales, const void* zeros,
+                          const hr_qspec* q, int64_t rows, int64_t n, const void* ref,
+                          int ref_dtype, float* deq, hr_dq_stats* stats, void* stream);
+
+/*
  * Randomised rotations: the rotation becomes R' = P . D_in . R . D_out with
  *   P      the permutation with (x . P)[j] = x[perm[j]] (a gather),
  *   D_in   diag(in_signs), D_out = diag(out_signs) (+-1 entries),

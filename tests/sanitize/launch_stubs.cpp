@@ -13,6 +13,7 @@ int launch_colrot(const ColArgs&, void*) { return static_cast<int>(hipErrorNoDev
 int launch_fast(const FastKey&, const FastArgs&, void*) { return -static_cast<int>(hipErrorNoDevice); }
 int launch_kron(const FastKey&, const KronArgs&, void*) { return -static_cast<int>(hipErrorNoDevice); }
 int launch_dequant(const DqArgs&, void*) { return static_cast<int>(hipErrorNoDevice); }
+int scratch_address(void**) { return static_cast<int>(hipErrorNoDevice); }
 }  // namespace hr
 
 extern "C" {
