@@ -22,6 +22,7 @@
 
 namespace hr {
 bool paley_matrix(int k, std::vector<int8_t>& h);
+bool paley_character(int k, uint32_t* bits, int words);
 int64_t kron_order(int64_t n);
 }  // namespace hr
 
@@ -145,6 +146,12 @@ int check_block(int64_t n, int64_t block, Geometry* g) {
     if (k > hr::kMaxKron)
         return fail(HR_EUNSUPPORTED, "Kronecker base order %lld for n = %lld exceeds %d", (long long)k,
                     (long long)n, hr::kMaxKron);
+    if (k > hr::kMaxKronDense) {
+        uint32_t chi[hr::kMaxKron / 32];
+        if (!hr::paley_character(static_cast<int>(k), chi, hr::kMaxKron / 32))
+            return fail(HR_EUNSUPPORTED, "Kronecker base order %lld for n = %lld: orders above %d need a prime q = K - 1",
+                        (long long)k, (long long)n, hr::kMaxKronDense);
+    }
     if (n > 32768) return fail(HR_EUNSUPPORTED, "Kronecker rotation of n = %lld exceeds 32768", (long long)n);
     g->kron_k = static_cast<int>(k);
     g->block = n / k;
@@ -227,9 +234,11 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
     p->nt = static_cast<int>(nt);
     p->grid = (total_chunks + cpw - 1) / cpw;
     if (p->grid > 0x7FFFFFFF) return fail(HR_EUNSUPPORTED, "grid too large");
-    if (geo.kron_k) p->kmax = geo.kron_k <= 16 ? 16 : (geo.kron_k <= 32 ? 32 : 64);
+    if (geo.kron_k)
+        p->kmax = geo.kron_k <= 16 ? 16 : (geo.kron_k <= 32 ? 32 : (geo.kron_k <= hr::kMaxKronDense ? 64 : -1));
     const int64_t wg_elems = nt * e;
     size_t lds = static_cast<size_t>(wg_elems + (wg_elems >> 4)) * 4;  // padded transform buffer
+    if (p->kmax < 0) lds *= 2;                                          // wide Kronecker mix: output buffer
     lds += static_cast<size_t>(2 * (nt / 64 + 1)) * 4;                  // cross-wave reduction
     // zero-point staging: asymmetric groups at least a thread wide (smaller
     // groups are whole in one thread, which writes their zero points itself)
@@ -257,7 +266,11 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
         a.q[i].scale_dtype = qs[i].scale_dtype;
         a.q[i].tscale = qs[i].tscale;
     }
-    if (geo.kron_k) {
+    if (geo.kron_k > hr::kMaxKronDense) {
+        if (!hr::paley_character(geo.kron_k, a.kron_chi, hr::kMaxKron / 32))
+            return fail(HR_EUNSUPPORTED, "no base matrix of order %d", geo.kron_k);
+        a.kron_q = geo.kron_k - 1;
+    } else if (geo.kron_k) {
         std::vector<int8_t> h;
         if (!hr::paley_matrix(geo.kron_k, h)) return fail(HR_EUNSUPPORTED, "no base matrix of order %d", geo.kron_k);
         for (int c = 0; c < geo.kron_k; ++c) {
@@ -317,7 +330,8 @@ int run(const hr::RotPlan& p, void* stream) {
         if (r < 0)
             return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));
     }
-    if (!generic_only && !mixed && p.bf16 && a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9 && a.nq <= 1) {
+    if (!generic_only && !mixed && p.bf16 && a.nq <= 1 &&
+        ((a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9) || (a.kron_k > 32 && a.logb == 7))) {
         hr::FastKey k{};
         hr::KronArgs ka{};
         k.logb = a.logb;
@@ -336,7 +350,9 @@ int run(const hr::RotPlan& p, void* stream) {
         ka.rows = a.total_chunks;
         ka.norm = a.norm;
         ka.k = a.kron_k;
-        for (int c = 0; c < a.kron_k; ++c) ka.hk_neg[c] = static_cast<uint32_t>(a.hk_neg[c]);
+        for (int c = 0; c < a.kron_k && c < hr::kMaxKronDense; ++c) ka.hk_neg[c] = a.hk_neg[c];
+        for (int i = 0; i < hr::kMaxKron / 32; ++i) ka.kron_chi[i] = a.kron_chi[i];
+        ka.kron_q = a.kron_q;
         const int r = hr::launch_kron(k, ka, stream);
         if (r == 1) return ok();
         if (r < 0)

@@ -818,10 +818,11 @@ __host__ __device__ constexpr int kron_elem(int m, int q) {
 
 // INT4 g128 epilogue of the lane's 64 consecutive columns (the other 64 of
 // the group in lane l ^ 32). Arithmetic as in epi_int. cp: the 32 code bytes;
-// gidx: group index; zslot: LDS byte for the zero point (asymmetric).
+// gidx: group index.  Returns the group's zero point (0 if symmetric); the
+// caller packs zero points.
 template <class Q>
-__device__ __forceinline__ void epi_kron(const float (&u)[64], float f, const QuantDev& q, uint8_t* cp, int64_t gidx,
-                                         bool valid, bool first, uint8_t* zslot) {
+__device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, const QuantDev& q, uint8_t* cp,
+                                             int64_t gidx, bool valid, bool first) {
     static_assert(Q::logg == 7, "groups of 128 columns");
     float s, zf = 0.0f;
     if constexpr (Q::sym) {
@@ -857,6 +858,7 @@ __device__ __forceinline__ void epi_kron(const float (&u)[64], float f, const Qu
     const float rs = __builtin_amdgcn_rcpf(s);
     const float inv = f * rs;
     uint32_t w[8];
+    uint32_t zret = 0;
     if constexpr (Q::sym) {
         const float off = kMagic + 8.0f;
 #pragma unroll
@@ -880,13 +882,14 @@ __device__ __forceinline__ void epi_kron(const float (&u)[64], float f, const Qu
             }
             w[m] = pack8(t);
         }
-        if (first) *zslot = static_cast<uint8_t>(zi);
+        zret = zi;
     }
     if (valid) {
         stg16(cp, u32x4_t{w[0], w[1], w[2], w[3]});
         stg16(cp + 16, u32x4_t{w[4], w[5], w[6], w[7]});
         if (first) static_cast<uint16_t*>(q.scales)[gidx] = static_cast<uint16_t>(sbits);
     }
+    return zret;
 }
 
 template <int K, bool WROT, class Q0>
@@ -921,7 +924,7 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
     for (int k = 0; k < 2; ++k) {
         const int e = tid + 256 * k;
         const int c = e & 31, g = (e >> 5) & 1, p = (e >> 6) & 3, h = e >> 8;
-        const uint32_t nb = a.hk_neg[c] >> (16 * h + 8 * g + 2 * p);
+        const uint32_t nb = static_cast<uint32_t>(a.hk_neg[c] >> (16 * h + 8 * g + 2 * p));
         smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
     }
 
@@ -986,7 +989,12 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
             }
         }
         if constexpr (Q0::fmt == 0)
-            epi_kron<Q0>(v, a.norm, a.q, a.q.codes + (e0 >> 1), e0 >> 7, valid, valid && g == 0, zbuf + 4 * c + w);
+        {
+            const uint32_t zi = epi_kron<Q0>(v, a.norm, a.q, a.q.codes + (e0 >> 1), e0 >> 7, valid, valid && g == 0);
+            if constexpr (!Q0::sym) {
+                if (valid && g == 0) zbuf[4 * c + w] = static_cast<uint8_t>(zi);
+            }
+        }
         __syncthreads();   // operand reads and zero-point bytes done
         if constexpr (Q0::fmt == 0 && !Q0::sym) {
             // zero points of groups (2i, 2i + 1) -> one byte: 2 per piece
@@ -998,6 +1006,163 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
         }
         row = next;
         if (row >= a.rows) break;
+    }
+}
+
+
+// ---------------------------------------------------------------- kkronw
+// H_K[r][c] == -1 for the base matrix of `a` (dense bits for K <= 64, else
+// the Paley I construction over the integers mod the prime q = K - 1: +1 on
+// the diagonal and in row 0, -1 in column 0 below it, else the quadratic
+// character of (r - c) mod q).
+__device__ __forceinline__ bool kron_minus(const KronArgs& a, int r, int c) {
+    if (a.kron_q == 0) return (a.hk_neg[c] >> r) & 1u;
+    if (r == c || r == 0) return false;
+    if (c == 0) return true;
+    int d = r - c;
+    if (d < 0) d += a.kron_q;
+    return ((a.kron_chi[d >> 5] >> (d & 31)) & 1u) == 0u;
+}
+
+// Rows of n = K * 128 bf16 with 32 < K <= 160 (AutoRound "Rotation
+// Transform", section 1.5: base orders such as 108 and 140 combined with a
+// Sylvester block of 128): y = x (H_K (x) H_128) / sqrt(n).  One workgroup of
+// NW = ceil(K / 32) waves per row, persistent over rows.  Write the row as
+// x[a][b] (piece a < K, column b < 128).
+// Staging: the row goes to LDS as 16 bytes per (piece octet, column), dword j
+//   holding pieces 2j, 2j + 1 of the octet (as in kkron); octets past K are
+//   zero.  Each wave stages four octets: lane (octet 4w + l / 16, columns
+//   8 (l % 16) .. + 7).
+// Mix: wave w owns output pieces c = 32 w + l % 32.  For each tile t of 32
+//   columns, v_mfma_f32_32x32x16_bf16 over the 16-piece halves h:
+//   D[col][c] += sum_a x[16 h + a][col] H_K[16 h + a][c], A = 32 columns by 16
+//   pieces (one 16-byte LDS read per lane), B = the +-1 slice of H_K, built
+//   once per wave and kept in registers.  Exact bf16 products, float32 sums.
+// Then the 128-point transform of each output piece: bits b0, b1, b3, b4
+//   (tile rows) and b5, b6 (tiles) are register butterflies, b2 one
+//   v_permlane32_swap stage, after which lane l holds the 64 consecutive
+//   columns of piece c with b6 = l / 32 (the layout of kkron).
+// Epilogue: INT g128 = one piece per group (lanes l, l ^ 32); zero points of
+//   pieces c, c + 1 (lanes l, l ^ 1) share a byte.
+template <int K, bool WROT, class Q0>
+__global__ void __launch_bounds__(64 * ((K + 31) / 32)) kkronw(const KronArgs a) {
+    static_assert(K > 32 && K <= 160 && K % 4 == 0, "base orders 36..160");
+    constexpr int M = 128;
+    constexpr int n = K * M;
+    constexpr int NW = (K + 31) / 32;
+    constexpr int KH = (K + 15) / 16;          // 16-piece halves of the contraction
+    constexpr int NOCT = 2 * KH;               // staged octets
+    static_assert(NOCT <= 4 * NW, "each wave stages four octets");
+    __shared__ u32x4_t stage[NOCT * M];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = 32 * w + (lane & 31);         // output piece
+    const int g = lane >> 5;
+    const bool valid = c < K;
+
+    // B operands: half h, lane (c, g): H_K[16 h + 8 g + t][c], t = 0..7
+    u32x4_t bop[KH];
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t d = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 16 * h + 8 * g + 2 * p + e;
+                const uint32_t bits = (r < K && valid) ? (kron_minus(a, r, c) ? 0xBF80u : 0x3F80u) : 0u;
+                d |= bits << (16 * e);
+            }
+            bop[h][p] = d;
+        }
+    }
+    // A operand bases: lane (i, g) of tile t reads octet 2 h + g at column
+    // i + 32 t, slot (col & ~7) + ((col & 7) ^ ((col >> 3) & 7)); the swizzle
+    // depends on t & 1 only
+    const int il = lane & 31;
+    const u32x4_t* ab[2];
+#pragma unroll
+    for (int t1 = 0; t1 < 2; ++t1) {
+        const int hs = ((il >> 3) + 4 * t1) & 7;
+        ab[t1] = stage + opaque(g * M + (il & ~7) + 32 * t1 + ((il & 7) ^ hs));
+    }
+    // staging role: octet so = 4 w + l / 16, columns 8 cg .. 8 cg + 7
+    const int so = 4 * w + (lane >> 4);
+    const int cg = lane & 15;
+    const bool stager = so < NOCT;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        if (stager) {
+            const uint16_t* src = static_cast<const uint16_t*>(a.x) + row * n + 8 * cg;
+            u32x4_t ld[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int pc = 8 * so + j;
+                ld[j] = pc < K ? ldg16(src + pc * M) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                u32x4_t o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(ld[2 * j + 1][cc >> 1], ld[2 * j][cc >> 1], sel);
+                stage[so * M + 8 * cg + (cc ^ (cg & 7))] = o;
+            }
+        }
+        __syncthreads();
+
+        f32x16_t d[4];   // tile t = b5 + 2 b6
+#pragma unroll
+        for (int h = 0; h < KH; ++h) {
+            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bop[h]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[t & 1][2 * h * M + 64 * (t >> 1)]);
+                if (h == 0)
+                    d[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16_t{}, 0, 0, 0);
+                else
+                    d[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, d[t], 0, 0, 0);
+            }
+        }
+        float v[64];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[16 * t + r] = d[t][r];
+        // v[16 t + r]: column b0, b1 = r & 3, b3, b4 = r >> 2, b5, b6 = t; b2 = lane / 32
+        bfly<64, 0x3Fu>(v);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            float x0 = v[j], x1 = v[j + 32];
+            swap_halves(x0, x1);      // (b6 = lane / 32; b2 = 0, 1)
+            v[j] = x0 + x1;
+            v[j + 32] = x0 - x1;
+        }
+        const int64_t e0 = row * n + c * M + 64 * g;
+        if constexpr (WROT) {
+            if (valid) {
+                uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    u32x4_t o;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        o[p] = bf16x2(v[kron_elem(m, 2 * p)] * a.norm, v[kron_elem(m, 2 * p + 1)] * a.norm);
+                    stg16(dst + 8 * m, o);
+                }
+            }
+        }
+        if constexpr (Q0::fmt == 0) {
+            const uint32_t zi = epi_kron<Q0>(v, a.norm, a.q, a.q.codes + (e0 >> 1), e0 >> 7, valid, valid && g == 0);
+            if constexpr (!Q0::sym) {
+                // pieces c, c + 1 (K even) -> one byte, written by the even one
+                const uint32_t zodd = dppu<kXor1>(zi);
+                if (valid && g == 0 && (c & 1) == 0)
+                    a.q.zeros[(row * K + c) >> 1] = static_cast<uint8_t>((zi & 0xFu) | ((zodd & 0xFu) << 4));
+            }
+        }
+        __syncthreads();   // operand reads done before the next row is staged
     }
 }
 
@@ -1183,6 +1348,28 @@ int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
 
+template <int K, bool WROT, class Q0>
+int try_kkronw(const FastKey& k, const KronArgs& a, hipStream_t s) {
+    if (a.k != K || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
+    constexpr int NT = 64 * ((K + 31) / 32);
+    static std::atomic<int> slots[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -static_cast<int>(hipErrorInvalidDevice);
+    int cap = slots[dev].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kkronw<K, WROT, Q0>, NT, 0) != hipSuccess)
+            return -static_cast<int>(hipErrorInvalidValue);
+        cap = cus * (per > 0 ? per : 1);
+        slots[dev].store(cap, std::memory_order_relaxed);
+    }
+    const int64_t grid = a.rows < cap ? a.rows : cap;
+    hipLaunchKernelGGL((kkronw<K, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 1 : -static_cast<int>(e);
+}
+
 using IS128B = QD<0, 1, 7, 1>;   // INT sym g128 bf16 scales
 using IA128B = QD<0, 0, 7, 1>;   // INT asym g128 bf16 scales
 using IS128F = QD<0, 1, 7, 0>;
@@ -1193,10 +1380,27 @@ using NV = QD<2, 1, 4, 3>;       // NVFP4
 }  // namespace
 int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (k.logb != 9) return 0;
     int r = 0;
 #define HR_TRY(expr) \
     if ((r = (expr)) != 0) return r
+    if (k.logb == 7) {
+        // rows of K x 128, 32 < K <= 160
+        HR_TRY((try_kkronw<108, false, IA128B>(k, a, s)));
+        HR_TRY((try_kkronw<108, false, IS128B>(k, a, s)));
+        HR_TRY((try_kkronw<108, true, QNone>(k, a, s)));
+        HR_TRY((try_kkronw<108, true, IA128B>(k, a, s)));
+        HR_TRY((try_kkronw<108, true, IS128B>(k, a, s)));
+        HR_TRY((try_kkronw<140, false, IA128B>(k, a, s)));
+        HR_TRY((try_kkronw<140, false, IS128B>(k, a, s)));
+        HR_TRY((try_kkronw<140, true, QNone>(k, a, s)));
+        HR_TRY((try_kkronw<140, true, IA128B>(k, a, s)));
+        HR_TRY((try_kkronw<140, true, IS128B>(k, a, s)));
+        HR_TRY((try_kkronw<60, false, IA128B>(k, a, s)));
+        HR_TRY((try_kkronw<60, false, IS128B>(k, a, s)));
+        HR_TRY((try_kkronw<60, true, QNone>(k, a, s)));
+        return 0;
+    }
+    if (k.logb != 9) return 0;
     HR_TRY((try_kkron<28, false, IA128B>(k, a, s)));
     HR_TRY((try_kkron<28, true, IA128B>(k, a, s)));
     HR_TRY((try_kkron<28, false, IS128B>(k, a, s)));

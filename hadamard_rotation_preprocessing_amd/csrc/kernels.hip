@@ -238,6 +238,49 @@ __device__ __forceinline__ void kron_mix(float (&v)[1 << LOGE], float* lds, int 
     for (int j = 0; j < E; ++j) v[j] = lds[lpad(tid * E + j)];
 }
 
+// H_K[r][c] == -1 for the Kronecker base matrix of `a`: the dense bits, or
+// for orders above 64 the Paley I construction over the integers mod a prime
+// q: +1 on the diagonal and in row 0, -1 in column 0 below it, else the
+// quadratic character of (r - c) mod q.
+__device__ __forceinline__ bool hk_minus(const RotArgs& a, int r, int c) {
+    if (a.kron_q == 0) return (a.hk_neg[c] >> r) & 1u;
+    if (r == c || r == 0) return false;
+    if (c == 0) return true;
+    int d = r - c;
+    if (d < 0) d += a.kron_q;
+    return ((a.kron_chi[d >> 5] >> (d & 31)) & 1u) == 0u;
+}
+
+// Kronecker mix for orders above 64: each of the chunk's threads computes
+// outputs (c, col) in turn from the K pieces staged in LDS, into a second
+// LDS buffer (`out`), so no output overwrites an input still to be read.
+template <int LOGE>
+__device__ __forceinline__ void kron_mix_wide(float (&v)[1 << LOGE], float* lds, float* out, int tid, const RotArgs& a) {
+    constexpr int E = 1 << LOGE;
+    const int K = a.kron_k;
+    const int M = 1 << a.logb;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) lds[lpad(tid * E + j)] = v[j];
+    __syncthreads();
+    const int cl = tid / a.tpc;
+    const int lt = tid - cl * a.tpc;
+    const int cbase = cl * a.chunk;
+    for (int idx = lt; idx < K * M; idx += a.tpc) {
+        const int c = idx >> a.logb;
+        const int col = idx & (M - 1);
+        float acc = 0.0f;
+        for (int r = 0; r < K; ++r) {
+            const float z = lds[lpad(cbase + r * M + col)];
+            acc += hk_minus(a, r, c) ? -z : z;
+        }
+        out[lpad(cbase + c * M + col)] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) v[j] = out[lpad(tid * E + j)];
+}
+
 // ---------------------------------------------------------------- epilogue
 
 // Several whole groups of G = 2^LOGG elements in one thread's E = 2^LOGE
@@ -497,7 +540,8 @@ __global__ void __launch_bounds__(1024) rot_kernel(const RotArgs a) {
     const int tid = static_cast<int>(threadIdx.x);
     const int nt = static_cast<int>(blockDim.x);
     float* lds = smem;
-    float* red = smem + lpad(nt * E);
+    float* lds2 = smem + lpad(nt * E);                          // wide Kronecker mix only
+    float* red = lds2 + (KMAX < 0 ? lpad(nt * E) : 0);
     int* zst = reinterpret_cast<int*>(red + 2 * (nt / 64 + 1));
 
     const int cl = tid / a.tpc;
@@ -533,6 +577,7 @@ __global__ void __launch_bounds__(1024) rot_kernel(const RotArgs a) {
     }
     fwht<LOGE>(v, lds, tid, a.logb);
     if constexpr (KMAX > 0) kron_mix<LOGE, KMAX>(v, lds, tid, a);
+    if constexpr (KMAX < 0) kron_mix_wide<LOGE>(v, lds, lds2, tid, a);
 #pragma unroll
     for (int j = 0; j < E; ++j) v[j] *= a.norm;
     if (a.out_signs && valid) {
@@ -699,6 +744,7 @@ hipError_t launch_k(const RotPlan& p, hipStream_t s) {
             case 16: return launch_inst<LOGE, BF16, 16>(p, s);
             case 32: return launch_inst<LOGE, BF16, 32>(p, s);
             case 64: return launch_inst<LOGE, BF16, 64>(p, s);
+            case -1: return launch_inst<LOGE, BF16, -1>(p, s);
             default: break;
         }
     }

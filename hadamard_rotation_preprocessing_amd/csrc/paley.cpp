@@ -140,6 +140,23 @@ bool paley_matrix(int k, std::vector<int8_t>& h) {
 }
 
 // Smallest supported order K = odd(n) 2^j dividing n; 0 if none.
+// For a prime q = k - 1 (= 3 mod 4): bit d of `bits` (d < q, words of 32)
+// is set iff d is a nonzero square mod q.  The Paley I matrix is then
+// H[r][c] = +1 for r == c or r == 0, -1 for c == 0 < r, and chi((r - c) mod
+// q) otherwise (the construction above with field elements = integers mod
+// q).  Returns false if q is not prime or the bits do not fit.
+bool paley_character(int k, uint32_t* bits, int words) {
+    int p, r;
+    const int q = k - 1;
+    if (!paley_exists(k) || !prime_power(q, &p, &r) || r != 1 || q > 32 * words) return false;
+    for (int w = 0; w < words; ++w) bits[w] = 0u;
+    for (int x = 1; x < q; ++x) {
+        const int d = static_cast<int>((static_cast<int64_t>(x) * x) % q);
+        bits[d >> 5] |= 1u << (d & 31);
+    }
+    return true;
+}
+
 int64_t kron_order(int64_t n) {
     if (n <= 0 || (n & (n - 1)) == 0) return 0;
     int64_t odd = n;

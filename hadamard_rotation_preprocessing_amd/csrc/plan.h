@@ -11,7 +11,8 @@ namespace hr {
 constexpr int kMaxDevices = 64;
 
 constexpr int kMaxQuant = 2;
-constexpr int kMaxKron = 64;   // largest Kronecker base order handled on the GPU
+constexpr int kMaxKron = 160;      // largest Kronecker base order handled on the GPU
+constexpr int kMaxKronDense = 64;  // orders up to this pass the whole base matrix
 
 // One quantizer epilogue, resolved to device pointers.
 struct QuantDev {
@@ -41,7 +42,13 @@ struct RotArgs {
     QuantDev q[kMaxQuant];
     // Kronecker base matrix, by output column c: bit a of hk_neg[c] set iff
     // H_K[a][c] == -1, so that y_c = sum_a H_K[a][c] z_a (y = H_K^T z).
-    uint64_t hk_neg[kMaxKron];
+    // Orders above kMaxKronDense (prime q = K - 1 only) pass the quadratic
+    // character of GF(q) instead: kron_q = q, bit d of kron_chi set iff d is
+    // a nonzero square mod q (the matrix then follows from the Paley I
+    // construction; kron_q = 0 means hk_neg holds the matrix).
+    uint64_t hk_neg[kMaxKronDense];
+    uint32_t kron_chi[kMaxKron / 32];
+    int32_t kron_q;
     // randomised rotation (all nullable): element j of a row reads
     // x[perm[j]], is multiplied by in_signs[j] before and out_signs[j] after
     // the rotation; row_n is the row width n
@@ -55,7 +62,8 @@ struct RotArgs {
 struct RotPlan {
     int bf16;        // input/output dtype is bfloat16
     int loge;        // log2 elements per thread
-    int kmax;        // 0, 16, 32, 64: register bound for the Kronecker mix
+    int kmax;        // 0, 16, 32, 64: register bound for the Kronecker mix;
+                     // -1: orders above 64, mixed through a second LDS buffer
     int nt;          // threads per workgroup
     int64_t grid;    // workgroups
     size_t lds_bytes;
@@ -107,16 +115,22 @@ struct FastArgs {
     int64_t row_blocks;
 };
 
-// Arguments of the specialised Kronecker kernel (rows of K * 512 bf16).
+// Arguments of the specialised Kronecker kernels (rows of K * 512 bf16 with
+// K <= 32, or K * 128 with 32 < K <= 160).
 struct KronArgs {
     const void* x;
     void* y_rot;              // nullable
     int64_t rows;
     int64_t total_groups;
-    float norm;               // 1/sqrt(K * 512)
-    int32_t k;                // base order, <= 32
+    float norm;               // 1/sqrt(K * M)
+    int32_t k;                // base order
     QuantDev q;
-    uint32_t hk_neg[32];      // bit a of hk_neg[c] set iff H_K[a][c] == -1
+    // base matrix as in RotArgs: bit a of hk_neg[c] set iff H_K[a][c] == -1
+    // (K <= 64), or the quadratic character of GF(q), q = kron_q = K - 1
+    // prime (K > 64)
+    uint64_t hk_neg[kMaxKronDense];
+    uint32_t kron_chi[kMaxKron / 32];
+    int32_t kron_q;
 };
 
 // Compile-time shape of a specialised kernel, matched at dispatch.

@@ -88,7 +88,7 @@ extern "C" {
 typedef enum hr_status {
     HR_OK = 0,
     HR_EINVAL = -1,        /* bad argument: NULL, size, layout, alignment, aliasing */
-    HR_EUNSUPPORTED = -2,  /* well-formed but not implemented (bits != 4, K > 64, ...) */
+    HR_EUNSUPPORTED = -2,  /* well-formed but not implemented (bits != 4, K > 160, ...) */
     HR_EDEVICE = -3        /* HIP runtime error while enqueueing */
 } hr_status;
 
@@ -149,7 +149,11 @@ typedef struct hr_dq_stats {
  *          Sylvester if n is a power of two (n <= 32768), else the Kronecker
  *          form n = K * 2^m with K the smallest supported order K = odd(n) 2^j
  *          dividing n that has a Paley I construction (K - 1 a prime power
- *          = 3 mod 4) and K <= 64, n <= 32768.
+ *          = 3 mod 4), K <= 160 (above 64: K - 1 prime, e.g. 108 and 140),
+ *          n <= 32768.  Specialised kernels take bfloat16 rows of K x 512
+ *          (K <= 32) and K x 128 (K = 60, 108, 140); other Kronecker shapes,
+ *          and float32, run the generic kernel, which for K > 64 needs LDS
+ *          for two copies of the row (about 18000 elements at most).
  * Output is rounded to `dtype` (nearest even).
  */
 int hadamard_rotate(const void* x, void* y, int dtype, int64_t rows, int64_t n,

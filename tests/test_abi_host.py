@@ -85,7 +85,7 @@ def msg():
     (dict(n=4097 * 2, block=0, qs=q(g=2)), L.HR_EUNSUPPORTED, "base Hadamard"),
     (dict(n=65536, block=0), L.HR_EUNSUPPORTED, "exceeds"),
     (dict(n=131072, block=65536), L.HR_EUNSUPPORTED, "exceeds 32768"),
-    (dict(n=128 * 108, block=0), L.HR_EUNSUPPORTED, "exceeds 64"),
+    (dict(n=244 * 64, block=0), L.HR_EUNSUPPORTED, "exceeds 160"),
 ])
 def test_rotate_quantize_act_validation(kw, status, text):
     st = rqa(**kw)
@@ -179,7 +179,10 @@ def test_check_shape_refusals():
     assert cs(n=32768, specs=[spec_int(32768, False)]) == L.HR_EUNSUPPORTED
     assert "threads" in msg()
     assert cs(n=32768, specs=[spec_int(32768, True)]) == L.HR_OK
-    assert cs(n=128 * 108, specs=[spec_int(128, True)]) == L.HR_EUNSUPPORTED
+    assert cs(n=128 * 108, specs=[spec_int(128, True)]) == L.HR_OK          # K = 108, q = 107 prime
+    assert cs(n=128 * 140, specs=[spec_int(128, False)]) == L.HR_OK         # K = 140, q = 139 prime
+    assert cs(n=244 * 64, specs=[spec_int(128, True)]) == L.HR_EUNSUPPORTED
+    assert "exceeds 160" in msg()
     assert cs(n=4096, block=3) == L.HR_EINVAL
     assert cs(n=4096, specs=[spec_int(128, True)], nq=3) == L.HR_EINVAL
     assert cs(dt=7) == L.HR_EINVAL
@@ -187,7 +190,7 @@ def test_check_shape_refusals():
     assert cs(rows=0, n=4096) == L.HR_OK
 
 
-@pytest.mark.parametrize("n", [14336, 96, 5120, 12, 20 * 32, 60 * 8])
+@pytest.mark.parametrize("n", [14336, 96, 5120, 12, 20 * 32, 60 * 8, 108 * 128, 140 * 128, 132 * 64])
 def test_kron_order_matches_oracle_factorisation(n):
     """The library's base matrix (its own Paley construction in C++) equals the
     oracle's (built independently in Python) and both factorisations agree."""

@@ -112,6 +112,26 @@ def test_kronecker_512_pieces(kernel_path, k, mode):
     run_act(x, n, 0, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=mode.endswith("+rot"))
 
 
+@pytest.mark.parametrize("k", [60, 108, 140])
+@pytest.mark.parametrize("mode", ["rotate", "sym", "asym", "asym+rot", "sym+rot"])
+def test_kronecker_128_pieces(kernel_path, k, mode):
+    """Widths K x 128 with base orders above 32 (the compiled wide Kronecker
+    shapes: 108 and 140, whose base matrices come from a prime q, and 60) in
+    every mode, on a row count that is not a multiple of the grid."""
+    n = k * 128
+    x = synth.gaussian((11, n), seed=8100 + k, dtype=torch.bfloat16)
+    x[2] *= 1e-3
+    x[5, :500] = 0.0
+    if mode == "rotate":
+        say("hadamard_rotate (Kronecker)", 11, n)
+        y = hr.rotate(x.to(DEV), 0)
+        torch.cuda.synchronize()
+        check_rotated(to_np64(y), oracle.rotate(x, n), "bf16")
+        return
+    sym = mode.startswith("sym")
+    run_act(x, n, 0, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=mode.endswith("+rot"))
+
+
 @pytest.mark.parametrize("y_rot", [False, True])
 def test_r3_reduced_query_key(kernel_path, y_rot):
     w = synth.WORKLOADS["r3"]
@@ -267,7 +287,8 @@ def test_group_sizes(g, sym):
     run_act(x, n, block, hr.QSpec("int", 4, g, sym, "f32"), y_rot=True)
 
 
-@pytest.mark.parametrize("n", [96, 12 * 256, 20 * 64, 28 * 512, 60 * 64, 44 * 32, 28 * 8])
+@pytest.mark.parametrize("n", [96, 12 * 256, 20 * 64, 28 * 512, 60 * 64, 44 * 32, 28 * 8, 108 * 128, 140 * 128,
+                               108 * 32, 140 * 64])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_kronecker_widths(n, dtype):
     x = synth.gaussian((19, n), seed=4000 + n, dtype=dtype)
