@@ -331,7 +331,7 @@ int run(const hr::RotPlan& p, void* stream) {
             return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(-r)));
     }
     if (!generic_only && !mixed && p.bf16 && a.nq <= 1 &&
-        ((a.kron_k > 0 && a.kron_k <= 32 && a.logb == 9) || (a.kron_k > 32 && a.logb == 7))) {
+        ((a.kron_k > 0 && a.kron_k <= 32 && a.logb >= 8 && a.logb <= 10) || (a.kron_k > 32 && a.logb == 7))) {
         hr::FastKey k{};
         hr::KronArgs ka{};
         k.logb = a.logb;

@@ -763,9 +763,11 @@ __device__ __forceinline__ float max_halves(float v) {
 //   two half-waves (v_permlane32_swap) for b2, after which lane l holds the
 //   64 consecutive columns of piece c with b6 = l / 32.
 // Epilogue: a group of 128 columns (b0..b6) sits in lanes l and l ^ 32.
-template <int W, int HALVES>
+template <int W, int HALVES, int LOGM>
 __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float (&v)[64]) {
-    constexpr int BT = 8192;                 // B table offset, dwords
+    constexpr int M = 1 << LOGM;
+    constexpr int U = M / 128;               // column blocks contracted on the MFMA
+    constexpr int BT = 16 * M;               // B table offset, dwords (after the staging)
     const int il = lane & 31;
     const int g = lane >> 5;
     // B operand: lane (c, g) element t = H_K[16 h + 8 g + t][c]
@@ -785,19 +787,19 @@ __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float 
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int hs = ((il >> 3) + 4 * blk) & 7;
-        ab[blk] = reinterpret_cast<const u32x4_t*>(smem + opaque(4 * (g * 512 + (il & ~7) + 32 * blk + ((il & 7) ^ hs))));
+        ab[blk] = reinterpret_cast<const u32x4_t*>(smem + opaque(4 * (g * M + (il & ~7) + 32 * blk + ((il & 7) ^ hs))));
     }
     f32x16_t d[4];   // tile blk + 2 b6
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const bool neg = __builtin_popcount(u & W) & 1;
+    for (int u = 0; u < U; ++u) {
+        const bool neg = __builtin_popcount(u & W) & 1;   // H_U[u][W]
 #pragma unroll
         for (int h = 0; h < HALVES; ++h) {
             const bf16x8_t B = __builtin_bit_cast(bf16x8_t, neg ? bn[h] : bp[h]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int blk = t & 1, b6 = t >> 1;
-                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[blk][2 * h * 512 + 64 * b6 + 128 * u]);
+                const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[blk][2 * h * M + 64 * b6 + 128 * u]);
                 if (u == 0 && h == 0)
                     d[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16_t{}, 0, 0, 0);
                 else
@@ -809,6 +811,20 @@ __device__ __forceinline__ void kkron_mix(const uint32_t* smem, int lane, float 
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[16 * t + r] = d[t][r];
+}
+
+// kkron_mix for the wave-uniform output block w: one instance per block,
+// so the signs H_U[u][w] are compile-time constants.
+template <int W, int NW, int HALVES, int LOGM>
+__device__ __forceinline__ void kkron_mix_sel(int w, const uint32_t* smem, int lane, float (&v)[64]) {
+    if constexpr (W + 1 < NW) {
+        if (w == W)
+            kkron_mix<W, HALVES, LOGM>(smem, lane, v);
+        else
+            kkron_mix_sel<W + 1, NW, HALVES, LOGM>(w, smem, lane, v);
+    } else {
+        kkron_mix<W, HALVES, LOGM>(smem, lane, v);
+    }
 }
 
 // Element index of column 8 m + q (m, q < 8) within the lane's 64-column run.
@@ -892,37 +908,43 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
     return zret;
 }
 
-template <int K, bool WROT, class Q0>
-__global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
+template <int K, int LOGM, bool WROT, class Q0>
+__global__ void __launch_bounds__(64 * (1 << LOGM) / 128, 16 * 128 / (1 << LOGM))
+kkron(const KronArgs a) {
     static_assert(K <= 32, "one MFMA K-padding of 32");
-    constexpr int M = 512;
+    static_assert(LOGM >= 8 && LOGM <= 10, "pieces of 256, 512 or 1024");
+    constexpr int M = 1 << LOGM;
+    constexpr int NW = M / 128;              // waves: one block of 128 output columns each
+    constexpr int NT = 64 * NW;
     constexpr int n = K * M;
     constexpr int HALVES = K > 16 ? 2 : 1;   // 16-piece halves of the contraction
-    constexpr int BT = 8192;                 // B table offset, dwords (staging below)
-    constexpr int ZB = BT + 512;             // zero-point bytes, 4 per piece
-    __shared__ uint32_t smem[ZB + 32];
+    constexpr int OCT = 2 * HALVES;          // staged piece octets
+    constexpr int BT = 16 * M;               // B table offset, dwords (staging below)
+    constexpr int ZB = BT + 512;             // zero-point bytes, NW per piece
+    __shared__ uint32_t smem[ZB + 8 * NW];
     uint8_t* zbuf = reinterpret_cast<uint8_t*>(smem + ZB);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const bool stager = w < 2 * HALVES;
 
-    // Wave w < 2 HALVES loads piece octet w of a row: columns 8 lane .. 8 lane + 7.
+    // Staging pairs (octet, run of 8 columns): OCT * M / 8 of them over NT
+    // threads (one each when OCT = 4, half the threads when OCT = 2).
+    const int so = tid / (M / 8);            // octet
+    const int cg = tid % (M / 8);            // columns 8 cg .. 8 cg + 7
+    const bool stager = so < OCT;
     u32x4_t ld[8];
     auto load = [&](int64_t r) {
-        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * n + 8 * lane;
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * n + 8 * cg;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (8 * w + j < K) ld[j] = ldg16(src + (8 * w + j) * M);
+            if (8 * so + j < K) ld[j] = ldg16(src + (8 * so + j) * M);
             else ld[j] = u32x4_t{0u, 0u, 0u, 0u};
         }
     };
 
     // B table entry e = lane' + 64 (p + 4 h): H_K[16 h + 8 g + 2p (+1)][c]
     // for c = lane' % 32, g = lane' / 32, as packed bf16 +-1. Never overwritten.
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int e = tid + 256 * k;
+    for (int e = tid; e < 512; e += NT) {
         const int c = e & 31, g = (e >> 5) & 1, p = (e >> 6) & 3, h = e >> 8;
         const uint32_t nb = static_cast<uint32_t>(a.hk_neg[c] >> (16 * h + 8 * g + 2 * p));
         smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
@@ -930,7 +952,7 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
 
     // Rows blockIdx.x, blockIdx.x + gridDim.x, ...  Each row is loaded just
     // before it is staged: without a prefetch the kernel fits 128 VGPRs, so
-    // four workgroups per CU hide one another's load latency.
+    // four waves per SIMD hide one another's load latency.
     int64_t row = blockIdx.x;
     const int64_t stride = gridDim.x;
     const int c = lane & 31;                   // piece
@@ -938,11 +960,11 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
     const bool valid = c < K;
     for (;;) {
         if (stager) load(row);
-        // ---- phase 1: stage the row (16-byte slot of column 8 lane + cc at
-        // 8 lane + (cc ^ (lane & 7)) within octet w)
+        // ---- phase 1: stage the row (16-byte slot of column 8 cg + cc at
+        // 8 cg + (cc ^ (cg & 7)) within octet so)
         if (stager) {
-            const int base = 16 * (w * 512 + 8 * lane);     // bytes
-            const int hs16 = 16 * (lane & 7);
+            const int base = 16 * (so * M + 8 * cg);     // bytes
+            const int hs16 = 16 * (cg & 7);
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
                 const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
@@ -957,12 +979,7 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
 
         // ---- phase 2: mix on the MFMA, six register stages, one across halves
         float v[64];
-        switch (w) {
-            case 0: kkron_mix<0, HALVES>(smem, lane, v); break;
-            case 1: kkron_mix<1, HALVES>(smem, lane, v); break;
-            case 2: kkron_mix<2, HALVES>(smem, lane, v); break;
-            default: kkron_mix<3, HALVES>(smem, lane, v); break;
-        }
+        kkron_mix_sel<0, NW, HALVES, LOGM>(w, smem, lane, v);
         // v[16 (blk + 2 b6) + r]: column b0, b1 = r & 3, b3, b4 = r >> 2, b5 = blk; b2 = lane / 32
         bfly<64, 0x3Fu>(v);
 #pragma unroll
@@ -988,27 +1005,26 @@ __global__ void __launch_bounds__(256, 4) kkron(const KronArgs a) {
                 }
             }
         }
-        if constexpr (Q0::fmt == 0)
-        {
+        if constexpr (Q0::fmt == 0) {
             const uint32_t zi = epi_kron<Q0>(v, a.norm, a.q, a.q.codes + (e0 >> 1), e0 >> 7, valid, valid && g == 0);
             if constexpr (!Q0::sym) {
-                if (valid && g == 0) zbuf[4 * c + w] = static_cast<uint8_t>(zi);
+                if (valid && g == 0) zbuf[NW * c + w] = static_cast<uint8_t>(zi);
             }
         }
         __syncthreads();   // operand reads and zero-point bytes done
         if constexpr (Q0::fmt == 0 && !Q0::sym) {
-            // zero points of groups (2i, 2i + 1) -> one byte: 2 per piece
-            if (w == 0 && lane < 2 * K) {
-                const int pc = lane >> 1, k2 = lane & 1;
-                const uint8_t* zp = zbuf + 4 * pc + 2 * k2;
-                a.q.zeros[((row * n) >> 8) + 2 * pc + k2] = static_cast<uint8_t>(zp[0] | (zp[1] << 4));
+            // zero points of groups (2i, 2i + 1) -> one byte: NW / 2 per piece
+            // (the groups of a piece are its NW column blocks, one per wave)
+            for (int b = tid; b < K * NW / 2; b += NT) {
+                const int pc = b / (NW / 2), k2 = b % (NW / 2);
+                const uint8_t* zp = zbuf + NW * pc + 2 * k2;
+                a.q.zeros[row * (K * NW / 2) + b] = static_cast<uint8_t>(zp[0] | (zp[1] << 4));
             }
         }
         row = next;
         if (row >= a.rows) break;
     }
 }
-
 
 // ---------------------------------------------------------------- kkronw
 // H_K[r][c] == -1 for the base matrix of `a` (dense bits for K <= 64, else
@@ -1326,9 +1342,10 @@ int try_kbsmall(const FastKey& k, const FastArgs& a, hipStream_t s) {
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
 
-template <int K, bool WROT, class Q0>
+template <int K, int LOGM, bool WROT, class Q0>
 int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
-    if (a.k != K || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
+    if (a.k != K || k.logb != LOGM || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
+    constexpr int NT = 64 * (1 << LOGM) / 128;
     // persistent grid: as many workgroups as the device holds at once
     static std::atomic<int> slots[kMaxDevices];
     int dev = 0;
@@ -1337,13 +1354,13 @@ int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
     if (cap == 0) {
         int cus = 0, per = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kkron<K, WROT, Q0>, 256, 0) != hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kkron<K, LOGM, WROT, Q0>, NT, 0) != hipSuccess)
             return -static_cast<int>(hipErrorInvalidValue);
         cap = cus * (per > 0 ? per : 1);
         slots[dev].store(cap, std::memory_order_relaxed);
     }
     const int64_t grid = a.rows < cap ? a.rows : cap;
-    hipLaunchKernelGGL((kkron<K, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kkron<K, LOGM, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
 }
@@ -1400,18 +1417,38 @@ int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
         HR_TRY((try_kkronw<60, true, QNone>(k, a, s)));
         return 0;
     }
-    if (k.logb != 9) return 0;
-    HR_TRY((try_kkron<28, false, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<28, true, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<28, false, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<28, true, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<28, true, QNone>(k, a, s)));
-    HR_TRY((try_kkron<12, false, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<12, false, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<12, true, QNone>(k, a, s)));
-    HR_TRY((try_kkron<20, false, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<20, false, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<20, true, QNone>(k, a, s)));
+    // rows of K x 512
+    HR_TRY((try_kkron<28, 9, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 9, true, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 9, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 9, true, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 9, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<12, 9, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 9, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 9, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<20, 9, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 9, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 9, true, QNone>(k, a, s)));
+    // rows of K x 256 (e.g. 5120 = 20 x 256)
+    HR_TRY((try_kkron<20, 8, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 8, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 8, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<12, 8, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 8, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 8, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<28, 8, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 8, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 8, true, QNone>(k, a, s)));
+    // rows of K x 1024 (e.g. 12288 = 12 x 1024)
+    HR_TRY((try_kkron<12, 10, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 10, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<12, 10, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<20, 10, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 10, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<20, 10, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<28, 10, false, IA128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 10, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<28, 10, true, QNone>(k, a, s)));
 #undef HR_TRY
     return 0;
 }

@@ -94,12 +94,15 @@ def test_r4_kronecker_reduced_rows(kernel_path, y_rot):
     run_act(x, w.n, w.block, hr.QSpec.from_dict(w.qspecs[0]), y_rot=y_rot)
 
 
+@pytest.mark.parametrize("m", [256, 512, 1024])
 @pytest.mark.parametrize("k", [12, 20, 28])
 @pytest.mark.parametrize("mode", ["rotate", "sym", "asym", "asym+rot", "sym+rot"])
-def test_kronecker_512_pieces(kernel_path, k, mode):
-    """Widths K x 512 (the compiled Kronecker shapes) in every mode."""
-    n = k * 512
-    x = synth.gaussian((9, n), seed=8000 + k, dtype=torch.bfloat16)
+def test_kronecker_pieces(kernel_path, k, m, mode):
+    """Widths K x M with K <= 32 and pieces of M = 256, 512, 1024 (the
+    compiled Kronecker shapes, e.g. 20 x 256 = 5120, 28 x 512 = 14336,
+    12 x 1024 = 12288) in every mode."""
+    n = k * m
+    x = synth.gaussian((9, n), seed=8000 + k + m, dtype=torch.bfloat16)
     x[2] *= 1e-3
     x[5, :700] = 0.0
     if mode == "rotate":
