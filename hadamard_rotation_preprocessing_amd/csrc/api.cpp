@@ -706,22 +706,64 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
         return fail(HR_EINVAL, "block = %lld is not a power of two", (long long)block);
     if (out_features % b)
         return fail(HR_EINVAL, "block %lld does not divide out_features = %lld", (long long)b, (long long)out_features);
-    if (!is_pow2(b) || b < 32 || b > 4096)
-        return fail(HR_EUNSUPPORTED, "output-side rotation needs a power-of-two block of 32..4096 rows (got %lld)",
-                    (long long)b);
-    const int logb = ilog2(b);
-    // tile of b rows x C columns: C >= 8, b C = 2^14 where that allows (or
-    // the largest power of two below it that divides in_features, down to
-    // 2^11 elements)
-    constexpr int kColTileLog = 14;
-    int64_t C = int64_t{1} << (logb + 3 > kColTileLog ? 3 : kColTileLog - logb);
-    while (C > 8 && in_features % C) C >>= 1;
-    if (in_features % C || b * C < 2048)
-        return fail(HR_EUNSUPPORTED, "in_features = %lld must be a multiple of %lld for blocks of %lld rows",
-                    (long long)in_features, (long long)(2048 / b > 8 ? 2048 / b : 8), (long long)b);
-    if ((out_features / b) * (in_features / C) >= (int64_t{1} << 31))
-        return fail(HR_EINVAL, "tensor too large (out_features = %lld, in_features = %lld)", (long long)out_features,
-                    (long long)in_features);
+    hr::ColArgs a{};
+    if (is_pow2(b) && b >= 32 && b <= 4096) {
+        // colrot: tiles of b rows x C columns
+        const int logb = ilog2(b);
+        // tile of b rows x C columns: C >= 8, b C = 2^14 where that allows (or
+        // the largest power of two below it that divides in_features, down to
+        // 2^11 elements)
+        constexpr int kColTileLog = 14;
+        int64_t C = int64_t{1} << (logb + 3 > kColTileLog ? 3 : kColTileLog - logb);
+        while (C > 8 && in_features % C) C >>= 1;
+        if (in_features % C || b * C < 2048)
+            return fail(HR_EUNSUPPORTED, "in_features = %lld must be a multiple of %lld for blocks of %lld rows",
+                        (long long)in_features, (long long)(2048 / b > 8 ? 2048 / b : 8), (long long)b);
+        if ((out_features / b) * (in_features / C) >= (int64_t{1} << 31))
+            return fail(HR_EINVAL, "tensor too large (out_features = %lld, in_features = %lld)", (long long)out_features,
+                        (long long)in_features);
+        a.logb = logb;
+        a.strips = in_features / C;
+        a.tb = ilog2(b * C);
+    } else {
+        // colwide: tiles of all b = K M rows x 4 columns (a Sylvester block of
+        // 8192 rows, or the Kronecker form of a full-width b that is not a
+        // power of two)
+        int64_t K = 1, M = b;
+        if (!is_pow2(b)) {
+            if (block > 0) return fail(HR_EINVAL, "block = %lld is not a power of two", (long long)block);
+            K = hr::kron_order(b);
+            if (K == 0)
+                return fail(HR_EUNSUPPORTED, "no supported base Hadamard order for out_features = %lld", (long long)b);
+            M = b / K;
+        }
+        const bool shape_ok = (K == 1 && b == 8192) ||
+                              ((K == 12 || K == 20 || K == 28) && b <= 8192 && b % 512 == 0 && M >= 128);
+        if (!shape_ok)
+            return fail(HR_EUNSUPPORTED,
+                        "output-side rotation of %lld rows: blocks of 32..4096 or 8192 rows, or K x M rows with K "
+                        "12, 20 or 28, K M a multiple of 512 and at most 8192 (got K = %lld, M = %lld)",
+                        (long long)b, (long long)K, (long long)M);
+        if (in_features % 4)
+            return fail(HR_EUNSUPPORTED, "in_features = %lld must be a multiple of 4 for %lld rows",
+                        (long long)in_features, (long long)b);
+        if ((out_features / b) * (in_features / 4) >= (int64_t{1} << 31))
+            return fail(HR_EINVAL, "tensor too large (out_features = %lld, in_features = %lld)", (long long)out_features,
+                        (long long)in_features);
+        a.logb = ilog2(M);
+        a.strips = in_features / 4;
+        a.kron_k = static_cast<int32_t>(K);
+        if (K > 1) {
+            std::vector<int8_t> h;
+            if (!hr::paley_matrix(static_cast<int>(K), h)) return fail(HR_EUNSUPPORTED, "no base matrix of order %lld", (long long)K);
+            for (int o = 0; o < K; ++o) {
+                uint64_t m = 0;
+                for (int c = 0; c < K; ++c)
+                    if (h[static_cast<size_t>(c) * K + o] < 0) m |= uint64_t{1} << c;
+                a.hk_neg[o] = m;
+            }
+        }
+    }
     if ((st = check_ptr(w, "w", 16)) || (st = check_ptr(w_rot, "w_rot", 16))) return st;
     const size_t bytes = static_cast<size_t>(out_features * in_features) * dtype_size(dtype);
     if (w != w_rot) {
@@ -729,15 +771,11 @@ int rotate_fuse_weight_out(const void* w, int dtype, int64_t out_features, int64
         Range ry{"w_rot", reinterpret_cast<uintptr_t>(w_rot), reinterpret_cast<uintptr_t>(w_rot) + bytes};
         if (overlap(rw, ry)) return fail(HR_EINVAL, "w_rot partially overlaps w");
     }
-    hr::ColArgs a{};
     a.w = w;
     a.w_rot = w_rot;
     a.in = in_features;
     a.row_blocks = out_features / b;
-    a.strips = in_features / C;
     a.norm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
-    a.logb = logb;
-    a.tb = ilog2(b * C);
     a.bf16 = dtype == HR_BF16;
     const int e = hr::launch_colrot(a, stream);
     if (e != 0) return fail(HR_EDEVICE, "kernel launch failed: %s", hipGetErrorString(static_cast<hipError_t>(e)));

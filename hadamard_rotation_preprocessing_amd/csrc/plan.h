@@ -150,9 +150,14 @@ struct ColArgs {
     int64_t row_blocks;       // out_features / b
     int64_t strips;           // in_features / C
     float norm;               // 1 / sqrt(b)
-    int32_t logb;             // b = 2^logb, 5..12
-    int32_t tb;               // tile of 2^tb elements (b C), 11..15
+    int32_t logb;             // b = 2^logb, 5..12 (colrot); M = 2^logb (colwide)
+    int32_t tb;               // tile of 2^tb elements (b C), 11..15 (colrot)
     int32_t bf16;
+    // colwide (whole-height tiles of 4 columns): kron_k = K (1 for a
+    // Sylvester block of 8192) and the base matrix, bit c of hk_neg[a] set
+    // iff H_K[c][a] == -1
+    int32_t kron_k;
+    uint64_t hk_neg[32];
 };
 
 int launch_rotate(const RotPlan& p, void* stream);        // returns hipError_t

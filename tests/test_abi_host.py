@@ -243,7 +243,9 @@ def test_weight_out_validation():
     f = lib.rotate_fuse_weight_out
     assert f(A, L.HR_BF16, 4096, 4096, 3, B, None) == L.HR_EINVAL and "power of two" in msg()
     assert f(A, L.HR_BF16, 4096, 4096, 16, B, None) == L.HR_EUNSUPPORTED and "32..4096" in msg()
-    assert f(A, L.HR_BF16, 8192, 4096, 0, B, None) == L.HR_EUNSUPPORTED
+    assert f(A, L.HR_BF16, 16384, 4096, 0, B, None) == L.HR_EUNSUPPORTED      # taller than 8192 rows
+    assert f(A, L.HR_BF16, 10240, 4096, 0, B, None) == L.HR_EUNSUPPORTED      # 20 x 512 > 8192 rows
+    assert f(A, L.HR_BF16, 5120, 4098, 0, B, None) == L.HR_EUNSUPPORTED and "multiple of 4" in msg()
     assert f(A, L.HR_BF16, 96, 4096, 0, B, None) == L.HR_EUNSUPPORTED
     assert f(A, L.HR_BF16, 4096, 4096, 8192, B, None) == L.HR_EINVAL and "divide" in msg()
     assert f(A, L.HR_BF16, 4096, 100, 0, B, None) == L.HR_EUNSUPPORTED and "multiple" in msg()

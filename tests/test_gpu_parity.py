@@ -576,6 +576,28 @@ def test_weight_out_every_block(block):
     check_rotated(to_np64(wr).T.copy(), ref.T.copy(), "bf16")
 
 
+@pytest.mark.parametrize("out_f,in_f,block,dt", [(8192, 200, 0, "bf16"), (8192, 60, 0, "f32"), (16384, 36, 8192, "bf16"),
+                                                 (5120, 104, 0, "bf16"), (5120, 44, 0, "f32"), (1536, 100, 0, "bf16"),
+                                                 (2560, 64, 0, "bf16"), (3072, 52, 0, "bf16"), (3584, 68, 0, "bf16"),
+                                                 (6144, 36, 0, "bf16"), (7168, 40, 0, "bf16"), (7168, 12, 0, "f32")],
+                         ids=lambda v: str(v))
+def test_weight_out_tall_and_kronecker(out_f, in_f, block, dt):
+    """Output-side fusion over 8192 rows (Sylvester) and over out_features
+    that are not a power of two (the Kronecker form K x M: hidden 5120 =
+    20 x 256 and others), every column compared; in_features leave a ragged
+    number of 4-column tiles."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=out_f, in_features=in_f).to(dtype)
+    w[:, 3] = 0.0
+    say("rotate_fuse_weight_out", out_f, in_f, block, dt)
+    wr = hr.rotate_fuse_weight_out(w.to(DEV), block)
+    torch.cuda.synchronize()
+    ref = oracle.rotate_out(w, out_f, block)
+    rep = Report()
+    check_rotated(to_np64(wr).T.copy(), ref.T.copy(), dt, rep)
+    say("  ", rep)
+
+
 def test_weight_out_in_place_and_layer_equivalence():
     """In place, and the fused weight reproduces the rotated layer output:
     x . W'^T against (x . W^T) . R on the GPU-rounded weight."""
