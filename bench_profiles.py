@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Summaries of rocprofv3 runs of bench.py, as committed under profiles/.
+
+  python bench_profiles.py trace <kernel_trace.csv> <bench JSON line file>
+      per-part kernel durations, split by phase: the timed steps (launches
+      back to back, so neighbouring kernels overlap) and the event pass that
+      gives bench.py's per-part times; then the tiny workload's launches.
+  python bench_profiles.py traffic <fetch counter_collection.csv>
+      <write counter_collection.csv> <bench JSON line of the fetch run>
+      <out.txt> [traffic.json]
+      HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE run (KiB per
+      dispatch), scaled by what the same counters read for the runtime's
+      256 MiB device copy (bench.py --copy-calibration); appends the summary
+      to out.txt and writes traffic.json (stamped with the kernel sources'
+      digest, which bench.py checks before reporting roofline.traffic).
+  python bench_profiles.py sq <counter_collection.csv> <bench JSON line file>
+      per-part SQ counter averages with derived figures:
+        VALU instructions per wave = SQ_INSTS_VALU / SQ_WAVES;
+        VALU busy = SQ_ACTIVE_INST_VALU * 4 / (4 SIMDs * 256 CUs *
+          GRBM_GUI_ACTIVE / 8) (a wave64 instruction occupies its SIMD for 4
+          cycles; GRBM_GUI_ACTIVE is summed over the 8 XCDs);
+        wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.
+
+Launches are matched to bench.py's parts by order: the bench JSON line gives
+the parts, the steps and the warm-up steps run; each step launches every part
+once (warm-up, timed steps, event pass).
+"""
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+def cmd_trace(argv):
+    trace, bench = argv[0], argv[1]
+    d = json.loads(open(bench).read().strip().splitlines()[-1])
+    names = list(d["config"]["parts"].keys())
+    steps, warm = d["steps"], d["warmup_steps_run"]
+    rows = [r for r in csv.DictReader(open(trace)) if not r["Kernel_Name"].startswith(("__amd", "void at::"))]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    hot = rows[: (warm + 2 * steps) * len(names)]
+    per = {n: {"step": [], "event": [], "kernel": ""} for n in names}
+    for i, r in enumerate(hot):
+        step, k = divmod(i, len(names))
+        phase = "warm" if step < warm else ("step" if step < warm + steps else "event")
+        if phase == "warm":
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per[names[k]][phase].append(dur)
+        per[names[k]]["kernel"] = r["Kernel_Name"]
+    print("%-8s %6s %12s %12s %10s %10s  %s" % ("part", "calls", "step_avg_us", "event_avg_us", "event_min", "event_max",
+                                                "kernel"))
+    for n in names:
+        p = per[n]
+        ev = p["event"]
+        print("%-8s %6d %12.2f %12.2f %10.2f %10.2f  %s" % (n, len(p["step"]) + len(ev), statistics.mean(p["step"]),
+                                                            statistics.mean(ev), min(ev), max(ev), p["kernel"][:110]))
+    tail = rows[(warm + 2 * steps) * len(names):]
+    if tail:
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in tail]
+        print("tiny     %6d %12s %12.2f %10.2f %10.2f  %s" % (len(durs), "-", statistics.median(durs), min(durs),
+                                                               max(durs), tail[0]["Kernel_Name"][:110]))
+    print("bench: value %.1f GB/s, ms_per_step %.5f, sum of event-timed parts %.5f ms, warm-up %d steps in %.2f s"
+          % (d["value"], d["ms_per_step"], d["config"]["sum_of_parts_ms"], warm, d["warmup_s"]))
+
+
+COPY_KIB = 256 * 1024
+
+
+def sources_digest(root):
+    h = hashlib.sha256()
+    d = os.path.join(root, "hadamard_rotation_preprocessing_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def per_dispatch(path, counter):
+    vals = {}
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        vals[k] = vals.get(k, 0.0) + float(r["Counter_Value"])
+        names[k] = r["Kernel_Name"]
+    return [(names[k], vals[k]) for k in sorted(vals)]
+
+
+def split(disp, names, warm, steps):
+    hot = [d for d in disp if not d[0].startswith(("__amd", "void at::"))]
+    copies = [v for n, v in disp if n.startswith("__amd_rocclr_copyBuffer")]
+    out = {n: [] for n in names}
+    for i, (kn, v) in enumerate(hot[: (warm + 2 * steps) * len(names)]):
+        step, k = divmod(i, len(names))
+        if step >= warm:
+            out[names[k]].append(v)
+    return out, copies
+
+
+def cmd_traffic(argv):
+    fetch, write, bench, out_txt = argv[0:4]
+    out_json = argv[4] if len(argv) > 4 else None
+    d = json.loads(open(bench).read().strip().splitlines()[-1])
+    names = list(d["config"]["parts"].keys())
+    steps, warm = d["steps"], d["warmup_steps_run"]
+    fr, fc = split(per_dispatch(fetch, "FETCH_SIZE"), names, warm, steps)
+    wr, wc = split(per_dispatch(write, "WRITE_SIZE"), names, warm, steps)
+    rf = COPY_KIB / statistics.median(fc)
+    wf = COPY_KIB / statistics.median(wc)
+    root = os.path.dirname(os.path.abspath(__file__))
+    digest = sources_digest(root)
+    lines = ["copy calibration: FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB for %d KiB read and written -> "
+             "factors %.4f (read), %.4f (write)" % (statistics.median(fc), statistics.median(wc), COPY_KIB, rf, wf),
+             "kernel sources digest: %s" % digest, "",
+             "%-10s %14s %14s %14s %8s" % ("part", "read_bytes", "write_bytes", "alg_bytes", "ratio")]
+    kern = {}
+    for n in names:
+        rb = statistics.mean(fr[n]) * rf * 1024
+        wb = statistics.mean(wr[n]) * wf * 1024
+        alg = d["config"]["parts"][n]["bytes"]
+        lines.append("%-10s %14.0f %14.0f %14d %8.4f" % (n, rb, wb, alg, (rb + wb) / alg))
+        kern[n] = {"bytes_per_launch": int(round(rb + wb)), "read_bytes": int(round(rb)), "write_bytes": int(round(wb))}
+    open(out_txt, "a").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if out_json:
+        old = json.load(open(out_json)) if os.path.exists(out_json) else {}
+        if old.get("sources_digest") != digest:
+            old = {"kernels": {}}
+        old["sources_digest"] = digest
+        old.setdefault("kernels", {}).update(kern)
+        old["source"] = "profiles/traffic_hot_path_step.txt"
+        json.dump(old, open(out_json, "w"), indent=1)
+
+
+def cmd_sq(argv):
+    path, bench = argv[0], argv[1]
+    d = json.loads(open(bench).read().strip().splitlines()[-1])
+    names = list(d["config"]["parts"].keys())
+    steps, warm = d["steps"], d["warmup_steps_run"]
+    disp = {}
+    kname = {}
+    for r in csv.DictReader(open(path)):
+        k = int(r["Dispatch_Id"])
+        disp.setdefault(k, {})
+        disp[k][r["Counter_Name"]] = disp[k].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        kname[k] = r["Kernel_Name"]
+    order = [k for k in sorted(disp) if not kname[k].startswith(("__amd", "void at::"))]
+    per = {n: [] for n in names}
+    for i, k in enumerate(order[: (warm + 2 * steps) * len(names)]):
+        step, j = divmod(i, len(names))
+        if step >= warm:
+            per[names[j]].append(disp[k])
+    cu, simd = 256, 4
+    print("%-8s %9s %13s %10s %10s %9s %8s  %s" % ("part", "waves", "VALU/wave", "LDS/wave", "VALUbusy", "wait", "cycles",
+                                                  "counters (averages per dispatch)"))
+    for n in names:
+        avg = {c: statistics.mean(x[c] for x in per[n]) for c in per[n][0]}
+        w = avg.get("SQ_WAVES", 0.0)
+        busy = 100.0 * avg.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (simd * cu * avg["GRBM_GUI_ACTIVE"] / 8)
+        wait = 100.0 * avg.get("SQ_WAIT_INST_ANY", 0.0) / avg["SQ_WAVE_CYCLES"]
+        print("%-8s %9.0f %13.1f %10.1f %9.1f%% %8.1f%% %8.0f  %s" % (
+            n, w, avg["SQ_INSTS_VALU"] / w, avg.get("SQ_INSTS_LDS", 0.0) / w, busy, wait, avg["GRBM_GUI_ACTIVE"] / 8,
+            ", ".join("%s=%.0f" % (c, v) for c, v in sorted(avg.items()))))
+
+
+def main():
+    cmds = {"trace": cmd_trace, "traffic": cmd_traffic, "sq": cmd_sq}
+    if len(sys.argv) < 2 or sys.argv[1] not in cmds:
+        sys.exit(__doc__)
+    cmds[sys.argv[1]](sys.argv[2:])
+
+
+if __name__ == "__main__":
+    main()
