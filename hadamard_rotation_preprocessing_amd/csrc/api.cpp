@@ -301,7 +301,7 @@ int run(const hr::RotPlan& p, void* stream) {
     const bool signs_aligned =
         ((reinterpret_cast<uintptr_t>(a.in_signs) | reinterpret_cast<uintptr_t>(a.out_signs)) & 15) == 0;
     if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned &&
-        (a.logb == 4 || a.logb == 5 || a.logb == 7 || a.logb == 11 || a.logb == 12) &&
+        (a.logb == 4 || a.logb == 5 || a.logb == 7 || (a.logb >= 10 && a.logb <= 13)) &&
         a.chunk == (1 << a.logb)) {
         hr::FastKey k{};
         hr::FastArgs f{};

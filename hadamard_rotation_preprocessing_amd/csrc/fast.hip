@@ -387,10 +387,14 @@ __device__ __forceinline__ uint32_t sign_mask2(uint32_t s, int k) {
 
 template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
 __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
-    static_assert(LOGB == 11 || LOGB == 12, "4096 or 2048 blocks");
+    static_assert(LOGB >= 10 && LOGB <= 13, "blocks of 1024, 2048, 4096 or 8192");
+    static_assert(MIX == 0 || LOGB == 11 || LOGB == 12, "randomised rotations on 2048- and 4096-blocks");
     constexpr int E = KW::E, NC = KW::NC, NS = KW::NS, R = KW::R;
     constexpr int B = 1 << LOGB;
-    constexpr int BPW = 4096 / B;             // blocks per wave
+    // blocks of 8192: a pair of waves (w, w ^ 1) per block, each holding one
+    // half; index bit 12 is a butterfly across the pair through LDS
+    constexpr bool PAIR = LOGB == 13;
+    constexpr int BPW = PAIR ? 1 : 4096 / B;  // blocks per wave
     constexpr bool MIXED = MIX > 0;           // signs (1) or a permutation and signs (2)
     constexpr bool PERM = MIX == 2;
     // permutation: one workgroup per row of n <= 16384, staged in rowbuf, whose
@@ -430,6 +434,12 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         hi_ok = BPW == 1 || wv * BPW + 1 < rb;
         mcol[0] = wv * BPW * B;
         mcol[1] = mcol[0] + B;
+    } else if constexpr (PAIR) {
+        // both waves of a pair reach the exchange barriers: a pair past the
+        // end re-reads the last block and stores nothing
+        const int64_t blk = (static_cast<int64_t>(blockIdx.x) * 4 + wv) >> 1;
+        hi_ok = blk < a.units;
+        blk0 = hi_ok ? blk : a.units - 1;
     } else {
         const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wv;
         blk0 = wave * BPW;
@@ -444,10 +454,15 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         }
     }
     float* lds = PERM ? reinterpret_cast<float*>(rowbuf) + wv * KW::LDS : lds_all[wv];
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + blk0 * B;
-
-    // an absent second block re-reads the first (finite data, never stored)
-    const int hi_off = hi_ok ? 0 : 512 * (NC / 2);
+    // first element of the wave's 4096 (the wave's half of a block of 8192)
+    const int64_t ebase = blk0 * B + (PAIR ? 4096 * (wv & 1) : 0);
+    const uint16_t* src = static_cast<const uint16_t*>(a.x) + ebase;
+    // blocks of the wave that it stores: those before the end of the tensor
+    // (BPW > 1: the rest re-read the first block, finite data that is never
+    // stored); with a permutation, those inside the workgroup's row
+    const int64_t nvalid = BPW == 1 ? 1
+                         : PERM     ? (hi_ok ? 2 : 1)
+                                    : (a.units - blk0 < BPW ? a.units - blk0 : BPW);
     u32x4_t raw[NC];
     if constexpr (PERM) {
         // gather from the staged row: element j of the row is x[perm[j]]
@@ -471,7 +486,11 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         if (idle) return;  // whole wave idle; no barrier follows
     } else {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) raw[c] = ldg16(src + 512 * c + 8 * lane - (c < NC / 2 ? 0 : hi_off));
+        for (int c = 0; c < NC; ++c) {
+            constexpr int CPB = B / 512 < NC ? B / 512 : NC;      // chunks per block
+            const int kb = (512 * c) >> LOGB;                    // block of the chunk in the wave
+            raw[c] = ldg16(src + (kb < nvalid ? 512 * c : 512 * (c % CPB)) + 8 * lane);
+        }
     }
     if constexpr (MIXED) {
         if (a.in_signs) {
@@ -503,9 +522,9 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
             v[8 * c + 4 + j] = d1[j];
         }
     }
-    // register bits of L0: v-index bits 3..5 (e bits 9..11); e bit 11 only
-    // inside a 4096 block
-    bfly<E, (LOGB == 12) ? 0x38u : 0x18u>(v);
+    // register bits of L0: v-index bits 3..5 (e bits 9..11), those inside a
+    // block
+    bfly<E, (LOGB >= 12) ? 0x38u : (LOGB == 11 ? 0x18u : 0x08u)>(v);
 
     // transpose L0 -> lane-contiguous, in NS passes over r
     float y[E];
@@ -526,9 +545,26 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     }
     bfly<E, 0x38u>(y);                                   // bits 3, 4, 5
     dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);       // bit 6
+    if constexpr (PAIR) {
+        // bit 12 across the pair: four passes of 16 values per lane through
+        // the transpose buffers (value j of lane l at 65 j + l: no bank
+        // conflicts); wave w ^ 1 holds the same positions of the other half
+        const float* pl = lds_all[wv ^ 1];
+        const float sgn = (wv & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) lds[65 * j + lane] = y[16 * p + j];
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[16 * p + j] = fmaf(sgn, y[16 * p + j], pl[65 * j + lane]);
+            __syncthreads();
+        }
+    }
 
-    const bool valid = hi_ok || lane < 32;
-    const int64_t e0 = blk0 * B + static_cast<int64_t>(E) * lane;
+    // the lane's 64 elements lie in block (64 lane) >> LOGB of the wave
+    const bool valid = PAIR ? hi_ok : ((64 * lane) >> LOGB) < nvalid;
+    const int64_t e0 = ebase + static_cast<int64_t>(E) * lane;
     if constexpr (MIXED) {
         if (a.out_signs) {
             // the lane's 64 contiguous elements lie in one block
@@ -561,12 +597,13 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 #pragma unroll
         for (int m = 0; m < 32; ++m) lw[33 * lane + m] = bf16x2(y[2 * m], y[2 * m + 1]);
         wave_sync();
-        uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + blk0 * B;
+        uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + ebase;
         const int rb = 4 * lane + (lane >> 3);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const u32x4_t wv4 = {lw[rb + 264 * c], lw[rb + 264 * c + 1], lw[rb + 264 * c + 2], lw[rb + 264 * c + 3]};
-            if (c < NC / 2 || hi_ok) stg16(dst + 512 * c + 8 * lane, wv4);
+            const bool cvalid = PAIR ? hi_ok : ((512 * c) >> LOGB) < nvalid;
+            if (cvalid) stg16(dst + 512 * c + 8 * lane, wv4);
         }
         wave_sync();
     }
@@ -909,7 +946,7 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
 }
 
 template <int K, int LOGM, bool WROT, class Q0>
-__global__ void __launch_bounds__(64 * (1 << LOGM) / 128, 16 * 128 / (1 << LOGM))
+__global__ void __launch_bounds__(64 * (1 << LOGM) / 128, (16 * 128 >> LOGM) < 4 ? (16 * 128 >> LOGM) : 4)
 kkron(const KronArgs a) {
     static_assert(K <= 32, "one MFMA K-padding of 32");
     static_assert(LOGM >= 8 && LOGM <= 10, "pieces of 256, 512 or 1024");
@@ -1303,7 +1340,7 @@ template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
 int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
     if (k.logb != LOGB || k.wrot != (WROT ? 1 : 0) || k.mixed != MIX || !qmatch<Q0>(k, 0) || !qmatch<Q1>(k, 1))
         return 0;
-    constexpr int64_t bpw = 4096 >> LOGB;
+    constexpr int64_t bpw = LOGB <= 12 ? 4096 >> LOGB : 1;
     if constexpr (MIX == 2) {
         // one workgroup per row, its waves owning 4096 elements each
         if ((a.row_blocks << LOGB) > 16384 || (reinterpret_cast<uintptr_t>(a.perm) & 15) != 0) return 0;
@@ -1313,7 +1350,8 @@ int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? 1 : -static_cast<int>(e);
     }
-    const int64_t waves = (a.units + bpw - 1) / bpw;
+    // blocks of 8192: two waves per block
+    const int64_t waves = LOGB == 13 ? 2 * a.units : (a.units + bpw - 1) / bpw;
     const int64_t grid = (waves + 3) / 4;
     hipLaunchKernelGGL((kwave<LOGB, WROT, Q0, Q1, MIX>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
@@ -1475,6 +1513,20 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<11, false, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<11, true, QNone, QNone>(k, a, s)));
+    // 8192-wide blocks (a pair of waves per block)
+    HR_TRY((try_kwave<13, false, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<13, true, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<13, false, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<13, true, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<13, true, MX, IS128B>(k, a, s)));
+    HR_TRY((try_kwave<13, false, MX, IS128B>(k, a, s)));
+    HR_TRY((try_kwave<13, true, QNone, QNone>(k, a, s)));
+    // 1024-wide blocks (four per wave)
+    HR_TRY((try_kwave<10, false, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<10, true, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<10, false, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<10, true, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<10, true, QNone, QNone>(k, a, s)));
     // randomised rotations: signs (random Hadamard), permutation + signs (RPBH)
     HR_TRY((try_kwave<12, false, IS128B, QNone, 1>(k, a, s)));
     HR_TRY((try_kwave<12, false, IA128B, QNone, 1>(k, a, s)));

@@ -247,13 +247,16 @@ def test_weight_fusion_two_group_sizes_wide():
     check_nvfp4(out["quant"][1], y, rep)
 
 
-@pytest.mark.parametrize("block", [128, 2048, 4096])
+@pytest.mark.parametrize("block", [128, 1024, 2048, 4096, 8192])
 @pytest.mark.parametrize("sym", [True, False])
 @pytest.mark.parametrize("y_rot", [False, True])
 def test_specialised_shapes(kernel_path, block, sym, y_rot):
     """Every compiled shape of the specialised kernels (INT g128 bf16 scales),
-    on a row count that leaves the last wave partly empty."""
-    n = 8192
+    on a row count that leaves the last wave partly empty: 13 rows of 3072
+    hold 39 blocks of 1024 (the last wave has 3 of its 4), 13 rows of 8192 are
+    13 blocks of 8192 (the last workgroup's second wave pair lies past the
+    end)."""
+    n = 3072 if block == 1024 else 8192
     x = synth.gaussian((13, n), seed=2500 + block + sym, dtype=torch.bfloat16)
     x[3, :] *= 1e3
     x[4, 100:300] = 0.0
@@ -276,6 +279,26 @@ def test_weight_variants(kernel_path, w_rot, nq):
     check_mxfp4(out["quant"][0], y, rep)
     if nq == 2:
         check_int(out["quant"][1], y, 128, True, "bf16", rep)
+    say("  ", rep)
+
+
+@pytest.mark.parametrize("w_rot", [False, True])
+@pytest.mark.parametrize("rows", [1, 6])
+def test_weight_8192_wide(kernel_path, w_rot, rows):
+    """The weight pass on in_features 8192 (a pair of waves per row): W.H,
+    MXFP4 and int4 sym g128 from one read."""
+    w = synth.WORKLOADS["weight"]
+    W = synth.make_inputs(w, out_features=rows, in_features=8192)
+    specs = [hr.QSpec.from_dict(d) for d in w.qspecs]
+    say("rotate_fuse_weight", tuple(W.shape), specs, "w_rot", w_rot)
+    out = hr.rotate_fuse_weight(W.to(DEV), 0, specs, w_rot=w_rot)
+    torch.cuda.synchronize()
+    y = oracle.rotate(W, 8192)
+    rep = Report()
+    if w_rot:
+        check_rotated(to_np64(out["w_rot"]), y, "bf16", rep)
+    check_mxfp4(out["quant"][0], y, rep)
+    check_int(out["quant"][1], y, 128, True, "bf16", rep)
     say("  ", rep)
 
 
