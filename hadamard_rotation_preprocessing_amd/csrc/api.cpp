@@ -351,6 +351,28 @@ int run(const hr::RotPlan& p, void* stream) {
         ka.norm = a.norm;
         ka.k = a.kron_k;
         for (int c = 0; c < a.kron_k && c < hr::kMaxKronDense; ++c) ka.hk_neg[c] = a.hk_neg[c];
+        // Sylvester H_M = H_S (x) H_{M/S}, so H_K (x) H_M = (H_K (x) H_S) (x) H_{M/S}:
+        // the same row read as S K pieces of M / S.  Small base orders are
+        // regrouped this way while S K <= 32 and M / S >= 256, which halves the
+        // column blocks the MFMA contracts (and its work per row) at each step.
+        // H_K (x) H_S is -1 at (r, c) iff H_K is at (r / S, c / S) xor
+        // popcount(r & c & (S - 1)) is odd.
+        int sh = 0;
+        while (a.kron_k > 0 && (a.kron_k << (sh + 1)) <= 32 && a.logb - (sh + 1) >= 8) ++sh;
+        if (sh > 0) {
+            ka.k = a.kron_k << sh;
+            k.logb = a.logb - sh;
+            const int smask = (1 << sh) - 1;
+            for (int c = 0; c < ka.k; ++c) {
+                uint64_t m = 0;
+                for (int r = 0; r < ka.k; ++r) {
+                    const uint64_t base = (a.hk_neg[c >> sh] >> (r >> sh)) & 1u;
+                    const uint64_t sylv = static_cast<uint64_t>(__builtin_popcount(r & c & smask) & 1);
+                    m |= (base ^ sylv) << r;
+                }
+                ka.hk_neg[c] = m;
+            }
+        }
         for (int i = 0; i < hr::kMaxKron / 32; ++i) ka.kron_chi[i] = a.kron_chi[i];
         ka.kron_q = a.kron_q;
         const int r = hr::launch_kron(k, ka, stream);

@@ -954,8 +954,14 @@ kkron(const KronArgs a) {
     constexpr int NW = M / 128;              // waves: one block of 128 output columns each
     constexpr int NT = 64 * NW;
     constexpr int n = K * M;
-    constexpr int HALVES = K > 16 ? 2 : 1;   // 16-piece halves of the contraction
-    constexpr int OCT = 2 * HALVES;          // staged piece octets
+    // K <= 16: two rows per iteration, row r of the pair in piece slots
+    // 16 r .. 16 r + 15 (the lanes of a half-wave, and the MFMA's input and
+    // output dimensions), with H_K block-diagonal over the pair.  (The host
+    // regroups K x M as 2K x M / 2 where M / 2 >= 256, so this serves rows of
+    // K x 256, such as 3072 = 12 x 256.)
+    constexpr int PACK = K <= 16 ? 2 : 1;
+    constexpr int HALVES = 2;                // 16-slot halves of the contraction
+    constexpr int OCT = 4;                   // staged slot octets
     constexpr int BT = 16 * M;               // B table offset, dwords (staging below)
     constexpr int ZB = BT + 512;             // zero-point bytes, NW per piece
     __shared__ uint32_t smem[ZB + 8 * NW];
@@ -964,37 +970,52 @@ kkron(const KronArgs a) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
-    // Staging pairs (octet, run of 8 columns): OCT * M / 8 of them over NT
-    // threads (one each when OCT = 4, half the threads when OCT = 2).
+    // Staging pairs (slot octet, run of 8 columns): OCT * M / 8 of them, one
+    // per thread.  Slot s of an octet is piece s (PACK = 1) or piece s % 16 of
+    // row s / 16 of the pair (PACK = 2); slots without a piece stage zeros.
     const int so = tid / (M / 8);            // octet
     const int cg = tid % (M / 8);            // columns 8 cg .. 8 cg + 7
     const bool stager = so < OCT;
+    const int srow = PACK == 2 ? so >> 1 : 0;             // row of the pair
+    const int spc = PACK == 2 ? 8 * (so & 1) : 8 * so;    // first piece of the octet
     u32x4_t ld[8];
-    auto load = [&](int64_t r) {
-        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * n + 8 * cg;
+    auto load = [&](int64_t r0) {
+        const int64_t r = r0 + srow;
+        const bool rok = r < a.rows;
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + (rok ? r : r0) * n + 8 * cg;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (8 * so + j < K) ld[j] = ldg16(src + (8 * so + j) * M);
+            if (rok && spc + j < K) ld[j] = ldg16(src + (spc + j) * M);
             else ld[j] = u32x4_t{0u, 0u, 0u, 0u};
         }
     };
 
-    // B table entry e = lane' + 64 (p + 4 h): H_K[16 h + 8 g + 2p (+1)][c]
-    // for c = lane' % 32, g = lane' / 32, as packed bf16 +-1. Never overwritten.
+    // B table entry e = lane' + 64 (p + 4 h): slot 16 h + 8 g + 2p (+1) of
+    // input to slot c = lane' % 32 of output, g = lane' / 32, as packed bf16:
+    // H_K of the two pieces (+-1), or 0 across the rows of a pair.  Never
+    // overwritten.
     for (int e = tid; e < 512; e += NT) {
         const int c = e & 31, g = (e >> 5) & 1, p = (e >> 6) & 3, h = e >> 8;
-        const uint32_t nb = static_cast<uint32_t>(a.hk_neg[c] >> (16 * h + 8 * g + 2 * p));
-        smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
+        if (PACK == 2 && h != (c >> 4)) {
+            smem[BT + e] = 0u;
+        } else {
+            const int co = PACK == 2 ? c & 15 : c;
+            const int ri = PACK == 2 ? 8 * g + 2 * p : 16 * h + 8 * g + 2 * p;
+            const uint32_t nb = static_cast<uint32_t>(a.hk_neg[co] >> ri);
+            smem[BT + e] = 0x3F803F80u | ((nb & 1u) << 15) | ((nb & 2u) << 30);
+        }
     }
 
-    // Rows blockIdx.x, blockIdx.x + gridDim.x, ...  Each row is loaded just
-    // before it is staged: without a prefetch the kernel fits 128 VGPRs, so
-    // four waves per SIMD hide one another's load latency.
-    int64_t row = blockIdx.x;
-    const int64_t stride = gridDim.x;
-    const int c = lane & 31;                   // piece
+    // Rows (pairs of rows for PACK = 2) blockIdx.x, blockIdx.x + gridDim.x,
+    // ...  Each row is loaded just before it is staged: without a prefetch
+    // the kernel fits 128 VGPRs, so four waves per SIMD hide one another's
+    // load latency.
+    int64_t row = static_cast<int64_t>(blockIdx.x) * PACK;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * PACK;
+    const int c = lane & 31;                   // output slot
     const int g = lane >> 5;                   // column bit b6 after the mix
-    const bool valid = c < K;
+    const int pc = PACK == 2 ? c & 15 : c;     // piece of the slot
+    const int prow = PACK == 2 ? c >> 4 : 0;   // row of the pair
     for (;;) {
         if (stager) load(row);
         // ---- phase 1: stage the row (16-byte slot of column 8 cg + cc at
@@ -1028,7 +1049,8 @@ kkron(const KronArgs a) {
         }
         // v[j]: column 8 m + q of the run of 64 starting at 64 (g + 2 w),
         // with j = kron_elem(m, q)
-        const int64_t e0 = row * n + c * M + 64 * (g + 2 * w);
+        const bool valid = pc < K && row + prow < a.rows;
+        const int64_t e0 = (row + prow) * n + pc * M + 64 * (g + 2 * w);
         if constexpr (WROT) {
             if (valid) {
                 uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
@@ -1052,10 +1074,12 @@ kkron(const KronArgs a) {
         if constexpr (Q0::fmt == 0 && !Q0::sym) {
             // zero points of groups (2i, 2i + 1) -> one byte: NW / 2 per piece
             // (the groups of a piece are its NW column blocks, one per wave)
-            for (int b = tid; b < K * NW / 2; b += NT) {
-                const int pc = b / (NW / 2), k2 = b % (NW / 2);
-                const uint8_t* zp = zbuf + NW * pc + 2 * k2;
-                a.q.zeros[row * (K * NW / 2) + b] = static_cast<uint8_t>(zp[0] | (zp[1] << 4));
+            constexpr int ZR = K * NW / 2;     // zero bytes per row
+            for (int b = tid; b < PACK * ZR; b += NT) {
+                const int r = b / ZR, bb = b % ZR;
+                const int zpc = bb / (NW / 2), k2 = bb % (NW / 2);
+                const uint8_t* zp = zbuf + NW * (16 * r * (PACK - 1) + zpc) + 2 * k2;
+                if (row + r < a.rows) a.q.zeros[(row + r) * ZR + bb] = static_cast<uint8_t>(zp[0] | (zp[1] << 4));
             }
         }
         row = next;
@@ -1397,7 +1421,8 @@ int try_kkron(const FastKey& k, const KronArgs& a, hipStream_t s) {
         cap = cus * (per > 0 ? per : 1);
         slots[dev].store(cap, std::memory_order_relaxed);
     }
-    const int64_t grid = a.rows < cap ? a.rows : cap;
+    const int64_t units = K <= 16 ? (a.rows + 1) / 2 : a.rows;   // rows, or pairs of rows (K <= 16)
+    const int64_t grid = units < cap ? units : cap;
     hipLaunchKernelGGL((kkron<K, LOGM, WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
@@ -1461,9 +1486,9 @@ int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
     HR_TRY((try_kkron<28, 9, false, IS128B>(k, a, s)));
     HR_TRY((try_kkron<28, 9, true, IS128B>(k, a, s)));
     HR_TRY((try_kkron<28, 9, true, QNone>(k, a, s)));
-    HR_TRY((try_kkron<12, 9, false, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<12, 9, false, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<12, 9, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<24, 9, false, IA128B>(k, a, s)));   // 12 x 1024, regrouped
+    HR_TRY((try_kkron<24, 9, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<24, 9, true, QNone>(k, a, s)));
     HR_TRY((try_kkron<20, 9, false, IA128B>(k, a, s)));
     HR_TRY((try_kkron<20, 9, false, IS128B>(k, a, s)));
     HR_TRY((try_kkron<20, 9, true, QNone>(k, a, s)));
@@ -1474,13 +1499,13 @@ int launch_kron(const FastKey& k, const KronArgs& a, void* stream) {
     HR_TRY((try_kkron<12, 8, false, IA128B>(k, a, s)));
     HR_TRY((try_kkron<12, 8, false, IS128B>(k, a, s)));
     HR_TRY((try_kkron<12, 8, true, QNone>(k, a, s)));
+    HR_TRY((try_kkron<24, 8, false, IA128B>(k, a, s)));   // 12 x 512, regrouped
+    HR_TRY((try_kkron<24, 8, false, IS128B>(k, a, s)));
+    HR_TRY((try_kkron<24, 8, true, QNone>(k, a, s)));
     HR_TRY((try_kkron<28, 8, false, IA128B>(k, a, s)));
     HR_TRY((try_kkron<28, 8, false, IS128B>(k, a, s)));
     HR_TRY((try_kkron<28, 8, true, QNone>(k, a, s)));
-    // rows of K x 1024 (e.g. 12288 = 12 x 1024)
-    HR_TRY((try_kkron<12, 10, false, IA128B>(k, a, s)));
-    HR_TRY((try_kkron<12, 10, false, IS128B>(k, a, s)));
-    HR_TRY((try_kkron<12, 10, true, QNone>(k, a, s)));
+    // rows of K x 1024 (e.g. 20480 = 20 x 1024)
     HR_TRY((try_kkron<20, 10, false, IA128B>(k, a, s)));
     HR_TRY((try_kkron<20, 10, false, IS128B>(k, a, s)));
     HR_TRY((try_kkron<20, 10, true, QNone>(k, a, s)));

@@ -115,6 +115,23 @@ def test_kronecker_pieces(kernel_path, k, m, mode):
     run_act(x, n, 0, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=mode.endswith("+rot"))
 
 
+@pytest.mark.parametrize("rows", [1, 2, 3, 2501])
+@pytest.mark.parametrize("m", [256, 512, 1024])
+@pytest.mark.parametrize("mode", ["sym+rot", "asym+rot", "asym"])
+def test_kronecker_small_order(kernel_path, rows, m, mode):
+    """Base order 12.  Over pieces of 256 the kernel takes two rows per pass:
+    one row, a full pair, a pair missing its second row, and enough rows that
+    every workgroup handles several pairs and the last pair is again one
+    short.  Over 512 and 1024 the row is taken as 24 pieces of half the size
+    (H_12 (x) H_2 as the base matrix), on the same row counts."""
+    n = 12 * m
+    x = synth.gaussian((rows, n), seed=8200 + rows + m, dtype=torch.bfloat16)
+    if rows > 2:
+        x[rows - 1] *= 1e-3
+        x[1, :300] = 0.0
+    run_act(x, n, 0, hr.QSpec("int", 4, 128, mode.startswith("sym"), "bf16"), y_rot=mode.endswith("+rot"))
+
+
 @pytest.mark.parametrize("k", [60, 108, 140])
 @pytest.mark.parametrize("mode", ["rotate", "sym", "asym", "asym+rot", "sym+rot"])
 def test_kronecker_128_pieces(kernel_path, k, mode):
