@@ -601,6 +601,26 @@ def test_weight_out_fusion(shape):
     check_rotated(got.T.copy(), ref.T.copy(), dtname(w))
 
 
+@pytest.mark.parametrize("in_f,dt", [(6144, "bf16"), (8192, "bf16"), (10240, "bf16"), (12352, "bf16"),
+                                     (3080, "f32")])
+def test_weight_out_tiles_per_workgroup(in_f, dt):
+    """4096 rows in tiles of 8 columns on a grid of one workgroup per CU:
+    3, 4, 5, and 6 or 7 tiles per workgroup for bf16 (the two tiles before
+    the pair loop, whole pairs, an odd last tile), and a float32 weight.
+    Every column of a sample of 128 is compared."""
+    out_f = 4096
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=out_f, in_features=in_f)
+    w = w.float() if dt == "f32" else w
+    say("rotate_fuse_weight_out", out_f, in_f, 0, dt)
+    wr = hr.rotate_fuse_weight_out(w.to(DEV), 0)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(in_f - 8, in_f),
+                                     np.random.default_rng(in_f).choice(in_f, size=112, replace=False)]))
+    ref = oracle.rotate_out(w[:, torch.as_tensor(cols)], out_f, 0)
+    got = to_np64(wr)[:, cols]
+    check_rotated(got.T.copy(), ref.T.copy(), dt)
+
+
 @pytest.mark.parametrize("block", [32, 64, 128, 256, 512, 1024, 2048, 4096])
 def test_weight_out_every_block(block):
     """Every block size, with in_features three times the smallest tile width
