@@ -13,6 +13,13 @@
       256 MiB device copy (bench.py --copy-calibration); appends the summary
       to out.txt and writes traffic.json (stamped with the kernel sources'
       digest, which bench.py checks before reporting roofline.traffic).
+  python bench_profiles.py mem <SQ counter_collection.csv> <its bench JSON line file>
+      <TD/TA/TCP counter_collection.csv> <its bench JSON line file>
+      per-part memory-pipeline figures: vector memory instructions per wave;
+      TD busy and TD stalled by the L2 (TD_TD_BUSY, TD_TC_STALL) and TA
+      address stalls by the L2 (TA_ADDR_STALLED_BY_TC_CYCLES) as fractions
+      of 256 CUs x GRBM_GUI_ACTIVE / 8 cycles; L2 request latency in cycles
+      (TCP_TCC_*_REQ_LATENCY / TCP_TCC_*_REQ).
   python bench_profiles.py sq <counter_collection.csv> <bench JSON line file>
       per-part SQ counter averages with derived figures:
         VALU instructions per wave = SQ_INSTS_VALU / SQ_WAVES;
@@ -135,8 +142,9 @@ def cmd_traffic(argv):
         json.dump(old, open(out_json, "w"), indent=1)
 
 
-def cmd_sq(argv):
-    path, bench = argv[0], argv[1]
+def per_part_counters(path, bench):
+    """Counter values summed per dispatch, grouped by bench part (timed
+    steps and event pass; warm-up dispatches dropped): {part: [dict]}."""
     d = json.loads(open(bench).read().strip().splitlines()[-1])
     names = list(d["config"]["parts"].keys())
     steps, warm = d["steps"], d["warmup_steps_run"]
@@ -153,6 +161,13 @@ def cmd_sq(argv):
         step, j = divmod(i, len(names))
         if step >= warm:
             per[names[j]].append(disp[k])
+    return per
+
+
+def cmd_sq(argv):
+    path, bench = argv[0], argv[1]
+    per = per_part_counters(path, bench)
+    names = list(per)
     cu, simd = 256, 4
     print("%-8s %9s %13s %10s %10s %9s %8s  %s" % ("part", "waves", "VALU/wave", "LDS/wave", "VALUbusy", "wait", "cycles",
                                                   "counters (averages per dispatch)"))
@@ -166,8 +181,26 @@ def cmd_sq(argv):
             ", ".join("%s=%.0f" % (c, v) for c, v in sorted(avg.items()))))
 
 
+def cmd_mem(argv):
+    sq_path, sq_bench, t_path, t_bench = argv[:4]
+    a = {n: {c: statistics.mean(x[c] for x in v) for c in v[0]} for n, v in per_part_counters(sq_path, sq_bench).items()}
+    b = {n: {c: statistics.mean(x[c] for x in v) for c in v[0]} for n, v in per_part_counters(t_path, t_bench).items()}
+    cu = 256
+    print("%-8s %10s %10s %9s %9s %9s %9s %9s" % ("part", "VMEM_RD/wv", "VMEM_WR/wv", "TD busy", "TD<-TC", "TA<-TC",
+                                                   "L2 rd lat", "L2 wr lat"))
+    for n in a:
+        w = a[n]["SQ_WAVES"]
+        cyc = b[n]["GRBM_GUI_ACTIVE"] / 8
+        print("%-8s %10.2f %10.2f %8.1f%% %8.1f%% %8.1f%% %9.0f %9.0f" % (
+            n, a[n]["SQ_INSTS_VMEM_RD"] / w, a[n]["SQ_INSTS_VMEM_WR"] / w,
+            100.0 * b[n]["TD_TD_BUSY"] / (cu * cyc), 100.0 * b[n]["TD_TC_STALL"] / (cu * cyc),
+            100.0 * b[n]["TA_ADDR_STALLED_BY_TC_CYCLES"] / (cu * cyc),
+            b[n]["TCP_TCC_READ_REQ_LATENCY"] / max(b[n]["TCP_TCC_READ_REQ"], 1.0),
+            b[n]["TCP_TCC_WRITE_REQ_LATENCY"] / max(b[n]["TCP_TCC_WRITE_REQ"], 1.0)))
+
+
 def main():
-    cmds = {"trace": cmd_trace, "traffic": cmd_traffic, "sq": cmd_sq}
+    cmds = {"trace": cmd_trace, "traffic": cmd_traffic, "sq": cmd_sq, "mem": cmd_mem}
     if len(sys.argv) < 2 or sys.argv[1] not in cmds:
         sys.exit(__doc__)
     cmds[sys.argv[1]](sys.argv[2:])
