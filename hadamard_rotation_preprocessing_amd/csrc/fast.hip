@@ -1113,8 +1113,13 @@ __device__ __forceinline__ bool kron_minus(const KronArgs& a, int r, int c) {
 // Mix: wave w owns output pieces c = 32 w + l % 32.  For each tile t of 32
 //   columns, v_mfma_f32_32x32x16_bf16 over the 16-piece halves h:
 //   D[col][c] += sum_a x[16 h + a][col] H_K[16 h + a][c], A = 32 columns by 16
-//   pieces (one 16-byte LDS read per lane), B = the +-1 slice of H_K, built
-//   once per wave and kept in registers.  Exact bf16 products, float32 sums.
+//   pieces (one 16-byte LDS read per lane), B = the +-1 slice of H_K.  Exact
+//   bf16 products, float32 sums.  For these base orders (q = K - 1 prime)
+//   H_K is +1 in row 0, -1 in column 0 below it, and elsewhere a function
+//   of (r - c) mod q.  So lane (c, g)'s B for half h, H_K[16 h + 8 g + t][c]
+//   for t = 0..7, is one 16-byte entry of a table in LDS: entry o holds the
+//   signs at (r - c) mod q = o .. o + 7 (mod q), entry q is all -1 (column
+//   0), and row 0 is one element set to +1.  Rows past K meet zero A slots.
 // Then the 128-point transform of each output piece: bits b0, b1, b3, b4
 //   (tile rows) and b5, b6 (tiles) are register butterflies, b2 one
 //   v_permlane32_swap stage, after which lane l holds the 64 consecutive
@@ -1122,7 +1127,7 @@ __device__ __forceinline__ bool kron_minus(const KronArgs& a, int r, int c) {
 // Epilogue: INT g128 = one piece per group (lanes l, l ^ 32); zero points of
 //   pieces c, c + 1 (lanes l, l ^ 1) share a byte.
 template <int K, bool WROT, class Q0>
-__global__ void __launch_bounds__(64 * ((K + 31) / 32)) kkronw(const KronArgs a) {
+__global__ void __launch_bounds__(64 * ((K + 31) / 32), 4) kkronw(const KronArgs a) {
     static_assert(K > 32 && K <= 160 && K % 4 == 0, "base orders 36..160");
     constexpr int M = 128;
     constexpr int n = K * M;
@@ -1130,7 +1135,9 @@ __global__ void __launch_bounds__(64 * ((K + 31) / 32)) kkronw(const KronArgs a)
     constexpr int KH = (K + 15) / 16;          // 16-piece halves of the contraction
     constexpr int NOCT = 2 * KH;               // staged octets
     static_assert(NOCT <= 4 * NW, "each wave stages four octets");
+    constexpr int q = K - 1;
     __shared__ u32x4_t stage[NOCT * M];
+    __shared__ u32x4_t btab[K];                 // entries 0 .. q - 1: windows; q: column 0
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1138,22 +1145,28 @@ __global__ void __launch_bounds__(64 * ((K + 31) / 32)) kkronw(const KronArgs a)
     const int g = lane >> 5;
     const bool valid = c < K;
 
-    // B operands: half h, lane (c, g): H_K[16 h + 8 g + t][c], t = 0..7
-    u32x4_t bop[KH];
-#pragma unroll
-    for (int h = 0; h < KH; ++h) {
+    // the sign table (read after the first staging barrier)
+    for (int o = tid; o < K; o += 64 * NW) {
+        u32x4_t e;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            uint32_t d = 0;
+            uint32_t dw = 0;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int r = 16 * h + 8 * g + 2 * p + e;
-                const uint32_t bits = (r < K && valid) ? (kron_minus(a, r, c) ? 0xBF80u : 0x3F80u) : 0u;
-                d |= bits << (16 * e);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                int d = o + 2 * p + h2;
+                if (d >= q) d -= q;
+                // H_K at (1 + d, 1): the value at (r - c) mod q = d
+                const bool minus = o == q || kron_minus(a, 1 + d, 1);
+                dw |= (minus ? 0xBF80u : 0x3F80u) << (16 * h2);
             }
-            bop[h][p] = d;
+            e[p] = dw;
         }
+        btab[o] = e;
     }
+    // lane (c, g), half h: entry (16 h + 8 g - c) mod q, or q for column 0
+    // (stepped from o0 inside the mix, which keeps one register live)
+    int o0 = (8 * g - c) % q;
+    if (o0 < 0) o0 += q;
     // A operand bases: lane (i, g) of tile t reads octet 2 h + g at column
     // i + 32 t, slot (col & ~7) + ((col & 7) ^ ((col >> 3) & 7)); the swizzle
     // depends on t & 1 only
@@ -1190,9 +1203,14 @@ __global__ void __launch_bounds__(64 * ((K + 31) / 32)) kkronw(const KronArgs a)
         __syncthreads();
 
         f32x16_t d[4];   // tile t = b5 + 2 b6
+        int o = o0;
 #pragma unroll
         for (int h = 0; h < KH; ++h) {
-            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bop[h]);
+            u32x4_t bw = btab[c == 0 ? q : o];
+            o += 16;
+            if (o >= q) o -= q;
+            if (h == 0 && g == 0) bw[0] = (bw[0] & 0xFFFF0000u) | 0x3F80u;   // row 0: +1
+            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ab[t & 1][2 * h * M + 64 * (t >> 1)]);

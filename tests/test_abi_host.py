@@ -199,6 +199,23 @@ def test_kron_order_matches_oracle_factorisation(n):
     assert np.array_equal(h.astype(np.int64), oracle.paley_hadamard(k))
 
 
+@pytest.mark.parametrize("k", [60, 108, 140])
+def test_wide_base_matrices_are_bordered_circulants(k):
+    """The wide Kronecker kernel reads its +-1 operands from a table of
+    windows over one sequence, which relies on this shape of the library's
+    base matrices for prime q = K - 1 (AutoRound "Rotation Transform",
+    section 1.5): row 0 all +1, column 0 -1 below it, and the rest a
+    function of (r - c) mod q alone."""
+    kk, m, h = kron_order(k * 128, with_matrix=True)
+    assert (kk, m) == (k, 128)
+    h = h.astype(np.int64)
+    q = k - 1
+    assert np.all(h[0] == 1) and np.all(h[1:, 0] == -1)
+    r, c = np.meshgrid(np.arange(1, k), np.arange(1, k), indexing="ij")
+    seq = h[1:, 1][np.arange(q)]               # value at (r - c) mod q = d is h[1 + d][1]
+    assert np.array_equal(h[1:, 1:], seq[(r - c) % q])
+
+
 def test_kron_order_errors():
     lib = L.lib()
     K, M = ctypes.c_int32(), ctypes.c_int64()
