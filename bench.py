@@ -26,8 +26,8 @@ signs, blocks of 2048); down_out, the output-side fusion R1^T W on down_proj
 [4096, 14336]; r1_5120, R1 at hidden 5120 (Kronecker 20 x 256); r4_12288,
 r4_13824 and r4_17920, R4 at full intermediate widths 12 x 1024, 108 x 128
 and 140 x 128; out_5120 and out_8192, output-side fusion of square weights
-over 5120 (20 x 256) and 8192 rows; r1_8192, R1 at hidden 8192; r4_b1024, the
-R4 input with blocks of 1024.
+over 5120 (20 x 256) and 8192 rows; r1_8192, R1 at hidden 8192; r4_b1024,
+r4_b256 and r4_b64, the R4 input with blocks of 1024, 256 and 64.
 
 The step touches about 2 GB, eight times the 256 MB Infinity Cache, and no
 two launches read the same tensor, so every launch reads its input from HBM.
@@ -56,7 +56,7 @@ METRIC = "rotate+quantize GB/s and rows/s on 1 MI355X; fraction of HBM peak"
 PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
 EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_nv16", "r4_nv16", "r1_random", "r4_rpbh",
                "down_out", "r1_5120", "r4_12288", "r4_13824", "r4_17920", "out_5120",
-               "out_8192", "r1_8192", "r4_b1024")   # measured only when named in --only
+               "out_8192", "r1_8192", "r4_b1024", "r4_b256", "r4_b64")   # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -151,7 +151,8 @@ def build_parts(hr, synth, torch, only):
     # and R1 at hidden 8192 (blocks of 8192), R4 with blocks of 1024
     for name, wn, kw, block in (("r1_5120", "r1", dict(hidden=5120), 0), ("r4_12288", "r4", dict(inter=12288), 0),
                                 ("r4_13824", "r4", dict(inter=13824), 0), ("r4_17920", "r4", dict(inter=17920), 0),
-                                ("r1_8192", "r1", dict(hidden=8192), 0), ("r4_b1024", "r4", {}, 1024)):
+                                ("r1_8192", "r1", dict(hidden=8192), 0), ("r4_b1024", "r4", {}, 1024),
+                                ("r4_b256", "r4", {}, 256), ("r4_b64", "r4", {}, 64)):
         if only is not None and name in only:
             w = W[wn]
             x = synth.make_inputs(w, **kw)

@@ -284,9 +284,9 @@ int make_plan(int dtype, int64_t rows, int64_t n, const Geometry& geo, const QSp
 }
 
 // Specialised bf16 kernels (one wave per 128 blocks of 32 or 256 of 16, per eight rows of
-// 128, or per 4096 elements of 2048- or 4096-blocks; one workgroup per
-// Kronecker row of K x 512) take the call when one is compiled for its exact
-// shape (randomised rotations: kwave); the generic kernel runs
+// 128, or per 4096 elements of blocks of 64 and 256 .. 8192; one workgroup
+// per Kronecker row of K x M) take the call when one is compiled for its
+// exact shape (randomised rotations: kwave); the generic kernel runs
 // otherwise, or always after hr_set_generic_only(1).
 // Process-wide dispatch switch (hr_set_generic_only): 1 sends every call to
 // the generic kernel, so that tests can run each shape through both paths.
@@ -300,9 +300,10 @@ int run(const hr::RotPlan& p, void* stream) {
     // the specialised kernels read the sign vectors 8 and 16 bytes at a time
     const bool signs_aligned =
         ((reinterpret_cast<uintptr_t>(a.in_signs) | reinterpret_cast<uintptr_t>(a.out_signs)) & 15) == 0;
+    // (a chunk is one block, or for blocks smaller than a group several)
     if (!generic_only && p.bf16 && a.kron_k == 0 && signs_aligned &&
-        (a.logb == 4 || a.logb == 5 || a.logb == 7 || (a.logb >= 10 && a.logb <= 13)) &&
-        a.chunk == (1 << a.logb)) {
+        a.logb >= 4 && a.logb <= 13 &&
+        a.chunk % (1 << a.logb) == 0) {
         hr::FastKey k{};
         hr::FastArgs f{};
         k.logb = a.logb;
@@ -319,12 +320,12 @@ int run(const hr::RotPlan& p, void* stream) {
         }
         f.x = a.x;
         f.y_rot = a.y_rot;
-        f.units = a.total_chunks;
+        f.units = a.total_chunks * (a.chunk >> a.logb);   // blocks
         f.norm = a.norm;
         f.perm = a.perm;
         f.in_signs = a.in_signs;
         f.out_signs = a.out_signs;
-        f.row_blocks = a.row_n / a.chunk;
+        f.row_blocks = a.row_n >> a.logb;
         const int r = hr::launch_fast(k, f, stream);
         if (r == 1) return ok();
         if (r < 0)

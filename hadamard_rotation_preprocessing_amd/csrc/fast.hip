@@ -93,6 +93,7 @@ struct HSmallTable {
 };
 __constant__ constexpr HSmallTable<5> kH32 = HSmallTable<5>();
 __constant__ constexpr HSmallTable<4> kH16x2 = HSmallTable<4>();   // blockdiag(H_16, H_16)
+__constant__ constexpr HSmallTable<3> kH8x4 = HSmallTable<3>();    // blockdiag of four H_8
 
 template <int N, unsigned MASK>
 __device__ __forceinline__ void bfly(float (&v)[N]) {
@@ -350,7 +351,8 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A wave owns 4096 contiguous elements: one block of 4096 or two of 2048.
+// A wave owns 4096 contiguous elements: one block of 4096, or 4096 / B
+// blocks of B = 2048 .. 64 (half a block of 8192: a pair of waves).
 struct KW {
     static constexpr int E = 64;              // elements per lane
     static constexpr int NC = E / 8;          // 16-byte chunks per lane
@@ -368,8 +370,11 @@ struct KW {
 // bits {0, 1, 2, 7, 8}; register butterflies bits 9, 10 and (4096-blocks)
 // 11; an LDS transpose in NS
 // passes over r gives each lane 64 contiguous elements (L2); bits 3..5 are
-// then register bits and bit 6 is lane bit 0 (DPP).  For 2048-blocks bit 11
-// selects the block and is never mixed.
+// then register bits and bit 6 is lane bit 0 (DPP).  Bits at or above log2 B
+// select the block and are never mixed: 2048-blocks leave bit 11 alone,
+// 512-blocks bits 9..11, 256-blocks also bit 8 (the MFMA applies
+// blockdiag(H_16, H_16)), 64-blocks also bits 6, 7 (four H_8 on the MFMA, no
+// DPP stage).
 // Randomised rotation (MIX > 0): element j of a row reads x[perm[j]] and is
 // multiplied by in_signs[j] before and by out_signs[j] after the transform
 // (the random Hadamard H diag(+-1) of the AutoRound page, section 1.5;
@@ -387,7 +392,7 @@ __device__ __forceinline__ uint32_t sign_mask2(uint32_t s, int k) {
 
 template <int LOGB, bool WROT, class Q0, class Q1, int MIX = 0>
 __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
-    static_assert(LOGB >= 10 && LOGB <= 13, "blocks of 1024, 2048, 4096 or 8192");
+    static_assert(LOGB >= 6 && LOGB <= 13 && LOGB != 7, "blocks of 64, 256 .. 8192 (128: k128)");
     static_assert(MIX == 0 || LOGB == 11 || LOGB == 12, "randomised rotations on 2048- and 4096-blocks");
     constexpr int E = KW::E, NC = KW::NC, NS = KW::NS, R = KW::R;
     constexpr int B = 1 << LOGB;
@@ -484,12 +489,20 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         }
         __syncthreads();   // every gather done: rowbuf becomes the transpose buffers
         if (idle) return;  // whole wave idle; no barrier follows
-    } else {
+    } else if constexpr (LOGB >= 9) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             constexpr int CPB = B / 512 < NC ? B / 512 : NC;      // chunks per block
             const int kb = (512 * c) >> LOGB;                    // block of the chunk in the wave
             raw[c] = ldg16(src + (kb < nvalid ? 512 * c : 512 * (c % CPB)) + 8 * lane);
+        }
+    } else {
+        // blocks under 512: a chunk spans several blocks, so the test is per
+        // lane; a piece past the end re-reads its place in the first block
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = 512 * c + 8 * lane;
+            raw[c] = ldg16(src + ((e >> LOGB) < nvalid ? e : (e & (B - 1))));
         }
     }
     if constexpr (MIXED) {
@@ -507,7 +520,10 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         }
     }
 
-    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);   // hp[64]: row half 1
+    // the MFMA mixes index bits 0..2 with 7, 8 (H_32), with 7 only (blocks
+    // of 256: blockdiag(H_16, H_16)) or with neither (blocks of 64: four H_8)
+    const uint32_t* tw = LOGB >= 9 ? &kH32.w[0][lane][0] : (LOGB == 8 ? &kH16x2.w[0][lane][0] : &kH8x4.w[0][lane][0]);
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(tw);   // hp[64]: row half 1
     const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
     const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
     float v[E];
@@ -524,7 +540,7 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
     }
     // register bits of L0: v-index bits 3..5 (e bits 9..11), those inside a
     // block
-    bfly<E, (LOGB >= 12) ? 0x38u : (LOGB == 11 ? 0x18u : 0x08u)>(v);
+    bfly<E, (LOGB >= 12) ? 0x38u : (LOGB == 11 ? 0x18u : (LOGB == 10 ? 0x08u : 0u))>(v);
 
     // transpose L0 -> lane-contiguous, in NS passes over r
     float y[E];
@@ -544,7 +560,7 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         wave_sync();
     }
     bfly<E, 0x38u>(y);                                   // bits 3, 4, 5
-    dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);       // bit 6
+    if constexpr (LOGB >= 7) dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);   // bit 6
     if constexpr (PAIR) {
         // bit 12 across the pair: four passes of 16 values per lane through
         // the transpose buffers (value j of lane l at 65 j + l: no bank
@@ -602,7 +618,7 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const u32x4_t wv4 = {lw[rb + 264 * c], lw[rb + 264 * c + 1], lw[rb + 264 * c + 2], lw[rb + 264 * c + 3]};
-            const bool cvalid = PAIR ? hi_ok : ((512 * c) >> LOGB) < nvalid;
+            const bool cvalid = PAIR ? hi_ok : ((512 * c + (LOGB < 9 ? 8 * lane : 0)) >> LOGB) < nvalid;
             if (cvalid) stg16(dst + 512 * c + 8 * lane, wv4);
         }
         wave_sync();
@@ -1570,6 +1586,25 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<10, false, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<10, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<10, true, QNone, QNone>(k, a, s)));
+    // 512-, 256- and 64-wide blocks (8, 16 or 64 per wave)
+    HR_TRY((try_kwave<9, false, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<9, true, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<9, false, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<9, true, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<9, false, MX, QNone>(k, a, s)));
+    HR_TRY((try_kwave<9, true, QNone, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, false, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, true, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, false, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, true, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, false, MX, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, true, QNone, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, false, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, true, IA128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, false, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, true, IS128B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, false, MX, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, true, QNone, QNone>(k, a, s)));
     // randomised rotations: signs (random Hadamard), permutation + signs (RPBH)
     HR_TRY((try_kwave<12, false, IS128B, QNone, 1>(k, a, s)));
     HR_TRY((try_kwave<12, false, IA128B, QNone, 1>(k, a, s)));

@@ -264,20 +264,43 @@ def test_weight_fusion_two_group_sizes_wide():
     check_nvfp4(out["quant"][1], y, rep)
 
 
-@pytest.mark.parametrize("block", [128, 1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("block", [64, 128, 256, 512, 1024, 2048, 4096, 8192])
 @pytest.mark.parametrize("sym", [True, False])
 @pytest.mark.parametrize("y_rot", [False, True])
 def test_specialised_shapes(kernel_path, block, sym, y_rot):
     """Every compiled shape of the specialised kernels (INT g128 bf16 scales),
     on a row count that leaves the last wave partly empty: 13 rows of 3072
-    hold 39 blocks of 1024 (the last wave has 3 of its 4), 13 rows of 8192 are
-    13 blocks of 8192 (the last workgroup's second wave pair lies past the
-    end)."""
-    n = 3072 if block == 1024 else 8192
+    hold 39 blocks of 1024 (the last wave has 3 of its 4) and 9.75 waves of
+    blocks of 512, 256 or 64 (the last wave holds 3072 of its 4096
+    elements), and 13 rows of 8192 are 13 blocks of 8192 (the last
+    workgroup's second wave pair lies past the end)."""
+    n = 3072 if block in (64, 256, 512, 1024) else 8192
     x = synth.gaussian((13, n), seed=2500 + block + sym, dtype=torch.bfloat16)
     x[3, :] *= 1e3
     x[4, 100:300] = 0.0
     run_act(x, n, block, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=y_rot)
+
+
+@pytest.mark.parametrize("block", [64, 256, 512])
+@pytest.mark.parametrize("shape", [(13, 3072), (5, 192 * 4), (3, 512)], ids=["ragged-waves", "one-wave", "tiny"])
+@pytest.mark.parametrize("spec", ["mxfp4", "int-asym", "rotate"])
+def test_small_blocks(kernel_path, block, shape, spec):
+    """Blocks of 64, 256 and 512, several to a wave: MXFP4, INT asym with
+    groups spanning two 64-blocks, and rotation alone, on row counts that
+    fill a wave only partly (one wave of 3840 elements; 1536 elements)."""
+    rows, n = shape
+    if n % block:
+        pytest.skip("block does not divide n")
+    x = synth.gaussian((rows, n), seed=2700 + block + n, dtype=torch.bfloat16)
+    x[rows - 1, : min(n, 300)] = 0.0
+    if spec == "rotate":
+        say("hadamard_rotate", rows, n, "block", block)
+        y = hr.rotate(x.to(DEV), block)
+        torch.cuda.synchronize()
+        check_rotated(to_np64(y), oracle.rotate(x, n, block).reshape(-1, n), "bf16")
+        return
+    q = hr.QSpec.mxfp4() if spec == "mxfp4" else hr.QSpec("int", 4, 128, False, "bf16")
+    run_act(x, n, block, q, y_rot=spec == "int-asym")
 
 
 @pytest.mark.parametrize("w_rot", [False, True])
