@@ -314,7 +314,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path shards rows across GPUs with no communication, "
-              "and this build runs and reports a single MI355X (got --gpus %d)" % args.gpus, file=sys.stderr)
+              "so it runs and reports a single MI355X (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
