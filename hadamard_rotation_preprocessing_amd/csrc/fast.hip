@@ -272,6 +272,108 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
     }
 }
 
+// INT epilogue for groups smaller than the lane's E contiguous elements
+// (G = 32: two groups per lane; G = 16: four): each group's extremes,
+// scale, codes and zero point stay in the lane, with the arithmetic of
+// epi_int.  The lane's NG scales are one store, and its NG zero-point
+// nibbles (groups 2i, 2i + 1 share a byte, element order) one more.
+template <int E, class Q>
+__device__ __forceinline__ void epi_int_small(const float (&u)[E], float f, const QuantDev& q, int64_t e0,
+                                              bool valid) {
+    constexpr int G = 1 << Q::logg;
+    constexpr int NG = E / G;
+    static_assert(G >= 16 && G < E && NG <= 4, "two or four groups per lane");
+    uint32_t w[E / 8];
+    uint32_t sb[NG];
+    float sf[NG];
+    uint32_t zbits = 0;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const float* v = u + G * k;
+        float s, zf = 0.0f;
+        if constexpr (Q::sym) {
+            float am = fabsf(v[0]);
+#pragma unroll
+            for (int j = 1; j < G; ++j) am = fmaxf(am, fabsf(v[j]));
+            s = (am * f) * (1.0f / 7.0f);
+        } else {
+            float hi = v[0], nl = -v[0];
+#pragma unroll
+            for (int j = 1; j < G; ++j) {
+                hi = fmaxf(hi, v[j]);
+                nl = fmaxf(nl, -v[j]);
+            }
+            hi = fmaxf(hi, 0.0f) * f;
+            nl = fmaxf(nl, 0.0f) * f;  // -min(min y, 0)
+            s = (hi + nl) * (1.0f / 15.0f);
+            zf = nl;
+        }
+        uint32_t sbits = 0;
+        if constexpr (Q::sdt == 1) {
+            sbits = f2bf(s);
+            s = bf2f(sbits);
+            if (s == 0.0f) {
+                s = 1.0f;
+                sbits = 0x3F80u;
+            }
+        } else if (s == 0.0f) {
+            s = 1.0f;
+        }
+        sb[k] = sbits;
+        sf[k] = s;
+        const float rs = __builtin_amdgcn_rcpf(s);
+        const float inv = f * rs;
+        if constexpr (Q::sym) {
+            const float off = kMagic + 8.0f;
+#pragma unroll
+            for (int b = 0; b < G / 8; ++b) {
+                float t[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) t[j] = fmaf(v[8 * b + j], inv, off);
+                w[(G / 8) * k + b] = pack8(t) ^ 0x88888888u;
+            }
+        } else {
+            const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
+            const uint32_t zi = static_cast<uint32_t>(z);
+            const float lo = kMagic - z, hi = kMagic + 15.0f - z;
+#pragma unroll
+            for (int b = 0; b < G / 8; ++b) {
+                float t[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float r = __builtin_amdgcn_fmed3f(fmaf(v[8 * b + j], inv, kMagic), lo, hi);
+                    t[j] = __uint_as_float(__float_as_uint(r) + zi);
+                }
+                w[(G / 8) * k + b] = pack8(t);
+            }
+            zbits |= zi << (4 * k);
+        }
+    }
+    if (valid) {
+        uint8_t* cp = q.codes + (e0 >> 1);
+#pragma unroll
+        for (int b = 0; b < E / 32; ++b) stg16(cp + 16 * b, u32x4_t{w[4 * b], w[4 * b + 1], w[4 * b + 2], w[4 * b + 3]});
+        const int64_t g0 = e0 >> Q::logg;          // the lane's first group (a multiple of NG)
+        if constexpr (Q::sdt == 1) {
+            if constexpr (NG == 2) {
+                reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(q.scales) + g0)[0] = sb[0] | (sb[1] << 16);
+            } else {
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(q.scales) + g0) =
+                    u32x2_t{sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)};
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) static_cast<float*>(q.scales)[g0 + k] = sf[k];
+        }
+        if constexpr (!Q::sym) {
+            if constexpr (NG == 2)
+                q.zeros[g0 >> 1] = static_cast<uint8_t>(zbits);
+            else
+                *reinterpret_cast<uint16_t*>(q.zeros + (g0 >> 1)) = static_cast<uint16_t>(zbits);
+        }
+    }
+}
+
 // ----------------------------------------------------------- MXFP4 epilogue
 // Eight values -> eight E2M1 nibbles (element 0 lowest) with the hardware
 // converter, which divides by `sc`, rounds to nearest even and saturates.
@@ -336,7 +438,9 @@ __device__ __forceinline__ void epi_mxfp4(const float (&y)[E], const QuantDev& q
 template <int E, class Q>
 __device__ __forceinline__ void epilogue(const float (&u)[E], float f, const QuantDev& q, int64_t e0, bool valid,
                                          int lane, int64_t total_groups) {
-    if constexpr (Q::fmt == 0) {
+    if constexpr (Q::fmt == 0 && (1 << Q::logg) < E) {
+        epi_int_small<E, Q>(u, f, q, e0, valid);
+    } else if constexpr (Q::fmt == 0) {
         epi_int<E, Q>(u, f, q, e0, valid, lane, total_groups);
     } else if constexpr (Q::fmt == 1) {
         epi_mxfp4<E>(u, q, e0, valid);  // caller passes normalised values
@@ -1488,6 +1592,12 @@ using IS128B = QD<0, 1, 7, 1>;   // INT sym g128 bf16 scales
 using IA128B = QD<0, 0, 7, 1>;   // INT asym g128 bf16 scales
 using IS128F = QD<0, 1, 7, 0>;
 using IA128F = QD<0, 0, 7, 0>;
+using IS32B = QD<0, 1, 5, 1>;     // INT groups of 32, 64, 256 (bf16 scales)
+using IA32B = QD<0, 0, 5, 1>;
+using IS64B = QD<0, 1, 6, 1>;
+using IA64B = QD<0, 0, 6, 1>;
+using IS256B = QD<0, 1, 8, 1>;
+using IA256B = QD<0, 0, 8, 1>;
 using MX = QD<1, 1, 5, 2>;       // MXFP4
 using NV = QD<2, 1, 4, 3>;       // NVFP4
 
@@ -1586,6 +1696,19 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<10, false, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<10, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<10, true, QNone, QNone>(k, a, s)));
+    // INT groups of 32, 64 and 256 on 2048- and 4096-wide blocks
+    HR_TRY((try_kwave<11, false, IA32B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS32B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IA64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IA256B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<11, false, IS256B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA32B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IS32B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IS64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IA256B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<12, false, IS256B, QNone>(k, a, s)));
     // 512-, 256- and 64-wide blocks (8, 16 or 64 per wave)
     HR_TRY((try_kwave<9, false, IA128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<9, true, IA128B, QNone>(k, a, s)));

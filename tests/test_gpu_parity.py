@@ -281,6 +281,22 @@ def test_specialised_shapes(kernel_path, block, sym, y_rot):
     run_act(x, n, block, hr.QSpec("int", 4, 128, sym, "bf16"), y_rot=y_rot)
 
 
+@pytest.mark.parametrize("g", [32, 64, 256])
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("block", [2048, 4096])
+def test_int_group_sizes_bf16(kernel_path, g, sym, block):
+    """INT groups of 32 (two per lane), 64 and 256 on the 2048- and 4096-block
+    kernels: 13 rows of 6144 are 39 blocks of 2048 (the last wave holds one of
+    its two), and 13 rows of 8192 are 26 blocks of 4096 (the last workgroup
+    is half empty).  Rows of zeros and of large values exercise the scale's
+    edge cases."""
+    n = 6144 if block == 2048 else 8192
+    x = synth.gaussian((13, n), seed=2900 + g + block + sym, dtype=torch.bfloat16)
+    x[2] = 0.0
+    x[5, :1000] *= 1e4
+    run_act(x, n, block, hr.QSpec("int", 4, g, sym, "bf16"))
+
+
 @pytest.mark.parametrize("block", [64, 256, 512])
 @pytest.mark.parametrize("shape", [(13, 3072), (5, 192 * 4), (3, 512)], ids=["ragged-waves", "one-wave", "tiny"])
 @pytest.mark.parametrize("spec", ["mxfp4", "int-asym", "rotate"])
