@@ -355,21 +355,25 @@ __device__ __forceinline__ void epi_int_small(const float (&u)[E], float f, cons
         for (int b = 0; b < E / 32; ++b) stg16(cp + 16 * b, u32x4_t{w[4 * b], w[4 * b + 1], w[4 * b + 2], w[4 * b + 3]});
         const int64_t g0 = e0 >> Q::logg;          // the lane's first group (a multiple of NG)
         if constexpr (Q::sdt == 1) {
-            if constexpr (NG == 2) {
-                reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(q.scales) + g0)[0] = sb[0] | (sb[1] << 16);
+            // one store of the NG scales where the buffer's alignment allows it
+            // (the same for every lane: g0 is a multiple of NG), else NG
+            uint16_t* sp = static_cast<uint16_t*>(q.scales) + g0;
+            if ((reinterpret_cast<uintptr_t>(q.scales) & (2 * NG - 1)) == 0) {
+                if constexpr (NG == 2)
+                    *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 16);
+                else
+                    *reinterpret_cast<u32x2_t*>(sp) = u32x2_t{sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)};
             } else {
-                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(q.scales) + g0) =
-                    u32x2_t{sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)};
+#pragma unroll
+                for (int k = 0; k < NG; ++k) sp[k] = static_cast<uint16_t>(sb[k]);
             }
         } else {
 #pragma unroll
             for (int k = 0; k < NG; ++k) static_cast<float*>(q.scales)[g0 + k] = sf[k];
         }
         if constexpr (!Q::sym) {
-            if constexpr (NG == 2)
-                q.zeros[g0 >> 1] = static_cast<uint8_t>(zbits);
-            else
-                *reinterpret_cast<uint16_t*>(q.zeros + (g0 >> 1)) = static_cast<uint16_t>(zbits);
+            q.zeros[g0 >> 1] = static_cast<uint8_t>(zbits);
+            if constexpr (NG == 4) q.zeros[(g0 >> 1) + 1] = static_cast<uint8_t>(zbits >> 8);
         }
     }
 }
@@ -428,10 +432,18 @@ __device__ __forceinline__ void epi_mxfp4(const float (&y)[E], const QuantDev& q
 #pragma unroll
         for (int b = 0; b < E / 32; ++b) stg16(cp + 16 * b, u32x4_t{w[4 * b], w[4 * b + 1], w[4 * b + 2], w[4 * b + 3]});
         uint8_t* sp = static_cast<uint8_t*>(q.scales) + (e0 >> 5);
-        if constexpr (NB == 2)
-            *reinterpret_cast<uint16_t*>(sp) = static_cast<uint16_t>(ebytes);
-        else
+        if constexpr (NB == 2) {
+            // the E8M0 buffer need only be byte-aligned; e0 is a multiple of 64,
+            // so every lane's pair has the parity of the buffer
+            if ((reinterpret_cast<uintptr_t>(q.scales) & 1u) == 0) {
+                *reinterpret_cast<uint16_t*>(sp) = static_cast<uint16_t>(ebytes);
+            } else {
+                sp[0] = static_cast<uint8_t>(ebytes);
+                sp[1] = static_cast<uint8_t>(ebytes >> 8);
+            }
+        } else {
             *sp = static_cast<uint8_t>(ebytes);
+        }
     }
 }
 

@@ -44,11 +44,12 @@ def dtname(t):
     return "bf16" if t.dtype == torch.bfloat16 else "f32"
 
 
-def run_act(x, n, block, spec, y_rot=False, ref_y=None):
-    """Rotate+quantize x (CPU tensor [..., n]) on the GPU and check it."""
+def run_act(x, n, block, spec, y_rot=False, ref_y=None, out=None):
+    """Rotate+quantize x (CPU tensor [..., n]) on the GPU and check it
+    (into the caller's output buffers if `out` is given)."""
     say("rotate_quantize_act", tuple(x.shape), x.dtype, "block", block, spec)
     xg = x.to(DEV)
-    out = hr.rotate_quantize_act(xg, block, spec, y_rot=y_rot)
+    out = hr.rotate_quantize_act(xg, block, spec, y_rot=y_rot, out=out)
     torch.cuda.synchronize()
     y = oracle.rotate(x, n, block).reshape(-1, n) if ref_y is None else ref_y
     kk = oracle.kron_factor(n)[0] if (block <= 0 and n & (n - 1)) else 0
@@ -297,16 +298,47 @@ def test_int_group_sizes_bf16(kernel_path, g, sym, block):
     run_act(x, n, block, hr.QSpec("int", 4, g, sym, "bf16"))
 
 
+@pytest.mark.parametrize("case", ["mxfp4-4096", "int-g32-asym-2048", "int-g32-sym-4096"])
+def test_scale_buffers_at_minimum_alignment(kernel_path, case):
+    """Scale and zero-point buffers at the smallest alignment the C ABI
+    allows: E8M0 bytes at an odd address, bf16 scales at 2 mod 4 bytes, zero
+    points at an odd address.  Kernels that store a lane's scales at once
+    must fall back to naturally aligned pieces there."""
+    fmt, rest = case.split("-", 1)
+    if fmt == "mxfp4":
+        spec, block, n = hr.QSpec.mxfp4(), 0, 4096
+    else:
+        sym = "-sym-" in case
+        block = int(rest.rsplit("-", 1)[1])
+        spec, n = hr.QSpec("int", 4, 32, sym, "bf16"), (6144 if block == 2048 else 8192)
+    rows = 9
+    x = synth.gaussian((rows, n), seed=3300 + n + block, dtype=torch.bfloat16)
+    x[4] = 0.0
+    o = hr.alloc_quant_outputs(rows, n, spec, DEV)
+    gpr = n // spec.group_size
+    sbuf = torch.full((rows * gpr + 8,), 0, dtype=o["scales"].dtype, device=DEV)
+    o["scales"] = sbuf[1: 1 + rows * gpr].view(rows, gpr)
+    assert o["scales"].data_ptr() % (2 if o["scales"].element_size() == 1 else 4) != 0
+    if o["zeros"] is not None:
+        zbuf = torch.zeros(o["zeros"].numel() + 8, dtype=torch.uint8, device=DEV)
+        o["zeros"] = zbuf[1: 1 + o["zeros"].numel()]
+    run_act(x, n, block, spec, out=o)
+    torch.cuda.synchronize()
+    # nothing written outside the views
+    assert int(sbuf[0].view(torch.uint8 if sbuf.element_size() == 1 else torch.int16).item()) == 0
+    assert not sbuf[1 + rows * gpr:].view(torch.uint8).any()
+    if o["zeros"] is not None:
+        assert int(zbuf[0].item()) == 0 and not zbuf[1 + o["zeros"].numel():].any()
+
+
 @pytest.mark.parametrize("block", [64, 256, 512])
-@pytest.mark.parametrize("shape", [(13, 3072), (5, 192 * 4), (3, 512)], ids=["ragged-waves", "one-wave", "tiny"])
+@pytest.mark.parametrize("shape", [(13, 3072), (3, 1024), (3, 512)], ids=["ragged-waves", "one-wave", "tiny"])
 @pytest.mark.parametrize("spec", ["mxfp4", "int-asym", "rotate"])
 def test_small_blocks(kernel_path, block, shape, spec):
     """Blocks of 64, 256 and 512, several to a wave: MXFP4, INT asym with
     groups spanning two 64-blocks, and rotation alone, on row counts that
-    fill a wave only partly (one wave of 3840 elements; 1536 elements)."""
+    fill a wave only partly (3072 of its 4096 elements; 1536)."""
     rows, n = shape
-    if n % block:
-        pytest.skip("block does not divide n")
     x = synth.gaussian((rows, n), seed=2700 + block + n, dtype=torch.bfloat16)
     x[rows - 1, : min(n, 300)] = 0.0
     if spec == "rotate":
