@@ -1740,6 +1740,11 @@ int launch_fast(const FastKey& k, const FastArgs& a, void* stream) {
     HR_TRY((try_kwave<6, true, IS128B, QNone>(k, a, s)));
     HR_TRY((try_kwave<6, false, MX, QNone>(k, a, s)));
     HR_TRY((try_kwave<6, true, QNone, QNone>(k, a, s)));
+    // one group per block (R3 per head vector for head_dim 64 or 256)
+    HR_TRY((try_kwave<6, false, IA64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<6, false, IS64B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, false, IA256B, QNone>(k, a, s)));
+    HR_TRY((try_kwave<8, false, IS256B, QNone>(k, a, s)));
     // randomised rotations: signs (random Hadamard), permutation + signs (RPBH)
     HR_TRY((try_kwave<12, false, IS128B, QNone, 1>(k, a, s)));
     HR_TRY((try_kwave<12, false, IA128B, QNone, 1>(k, a, s)));

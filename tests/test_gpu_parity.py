@@ -298,6 +298,19 @@ def test_int_group_sizes_bf16(kernel_path, g, sym, block):
     run_act(x, n, block, hr.QSpec("int", 4, g, sym, "bf16"))
 
 
+@pytest.mark.parametrize("head_dim", [64, 256])
+@pytest.mark.parametrize("sym", [False, True])
+def test_r3_other_head_dims(kernel_path, head_dim, sym):
+    """R3 per head with one group per head vector for head_dim 64 and 256
+    (a block of the head size, quantized as one group), on a head count that
+    leaves the last wave partly filled."""
+    heads = 4096 // head_dim * 3 + 5
+    x = synth.gaussian((heads, head_dim), seed=3400 + head_dim + sym, dtype=torch.bfloat16)
+    x[7] = 0.0
+    x[9] *= 1e3
+    run_act(x, head_dim, 0, hr.QSpec("int", 4, head_dim, sym, "bf16"))
+
+
 @pytest.mark.parametrize("case", ["mxfp4-4096", "int-g32-asym-2048", "int-g32-sym-4096"])
 def test_scale_buffers_at_minimum_alignment(kernel_path, case):
     """Scale and zero-point buffers at the smallest alignment the C ABI
