@@ -35,9 +35,14 @@ Warm-up runs at least --warmup steps and at least --min-warmup-s seconds
 (both reported).  Timing uses HIP events on the stream the
 kernels are launched on (torch's current stream).  The value is algorithmic
 bytes (one read of each input plus every mandatory output write) per second
-over K whole steps with no event between launches; the per-part durations
-(and the roofline) come from K further steps with an event pair around each
-launch.  Prints one JSON line.
+over K whole steps with no event between launches.  The per-part durations
+(and the roofline) time each part alone: at least K launches back to back,
+each on the next of n copies of the part's input (n copies span at least
+640 MiB), one event pair around them all.  Each part's single-launch time
+inside K more steps, an event pair around every launch, is reported too
+(ms_single: it adds the events' few microseconds, which matter for the 42 MB
+R1 launch).  copy_reference times the runtime's 256 MiB device copy the same
+way, as a reference point.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -58,6 +63,7 @@ EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_nv16", "r4_nv16", "r1_random", "r4_rpbh
                "down_out", "r1_5120", "r4_12288", "r4_13824", "r4_17920", "out_5120",
                "out_8192", "r1_8192", "r4_b1024", "r4_b256", "r4_b64")   # measured only when named in --only
 COPY_BYTES = 256 * 1024 * 1024
+CYCLE_BYTES = 640 * 1024 * 1024   # input copies cycled per part when timing it alone
 
 
 def sources_digest() -> str:
@@ -92,7 +98,7 @@ def build_parts(hr, synth, torch, only):
         spec = hr.QSpec.from_dict(w.qspecs[0])
         xg = x.to(dev)
         out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-        parts["r1"] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out),
+        parts["r1"] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 0, spec, out=out),
                            bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
         host["r1"] = (x, w.n, 0, [spec], False)
     # block-32 rotation fused with MXFP4 on the R1 and R4 inputs: measured
@@ -104,7 +110,7 @@ def build_parts(hr, synth, torch, only):
             spec = hr.QSpec.mxfp4()
             xg = x.to(dev)
             out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 32, spec, out=out),
+            parts[name] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 32, spec, out=out),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
             host[name] = (x, w.n, 32, [spec], False)
     # block-16 rotation fused with NVFP4 (E4M3 block scales, unit tensor
@@ -116,7 +122,7 @@ def build_parts(hr, synth, torch, only):
             spec = hr.QSpec.nvfp4()
             xg = x.to(dev)
             out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 16, spec, out=out),
+            parts[name] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 16, spec, out=out),
                                bytes=x.numel() * 2 + x.numel() // 2 + x.numel() // 16, rows=x.shape[0])
     # randomised rotations (hr_mix): the random Hadamard H diag(+-1) on the R1
     # input, and RPBH (permutation, signs, blocks of 2048) on the R4 input
@@ -135,7 +141,7 @@ def build_parts(hr, synth, torch, only):
             if so:
                 mix["out_signs"] = synth.rademacher(w.n, 103).to(dev)
             out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec, block=block, mix=mix:
+            parts[name] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec, block=block, mix=mix:
                                hr.rotate_quantize_act(xg, block, spec, out=out, mix=mix),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], w.n, spec), rows=x.shape[0])
     # output-side fusion W' = R1^T W on down_proj [4096, 14336] (full width
@@ -143,7 +149,7 @@ def build_parts(hr, synth, torch, only):
     if only is not None and "down_out" in only:
         wd = synth.make_inputs(W["weight"], out_features=4096, in_features=14336).to(dev)
         yd = torch.empty_like(wd)
-        parts["down_out"] = dict(fn=lambda wd=wd, yd=yd: hr.rotate_fuse_weight_out(wd, 0, out=yd),
+        parts["down_out"] = dict(x=wd, fn=lambda wd=wd, yd=yd: hr.rotate_fuse_weight_out(wd, 0, out=yd),
                                  bytes=wd.numel() * 4, rows=wd.shape[0])
     # Kronecker widths of other model sizes: R1 at hidden 5120 (20 x 256),
     # R4 at full intermediate widths 12288 (12 x 1024), 13824 (108 x 128) and
@@ -160,14 +166,14 @@ def build_parts(hr, synth, torch, only):
             spec = hr.QSpec.from_dict(w.qspecs[0])
             xg = x.to(dev)
             out = hr.alloc_quant_outputs(x.shape[0], n, spec, dev)
-            parts[name] = dict(fn=lambda xg=xg, out=out, spec=spec, block=block:
+            parts[name] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec, block=block:
                                hr.rotate_quantize_act(xg, block, spec, out=out),
                                bytes=x.numel() * 2 + qbytes(x.shape[0], n, spec), rows=x.shape[0])
     for name, rows_out in (("out_5120", 5120), ("out_8192", 8192)):
         if only is not None and name in only:
             wo = synth.make_inputs(W["weight"], out_features=rows_out, in_features=rows_out).to(dev)
             yo = torch.empty_like(wo)
-            parts[name] = dict(fn=lambda wo=wo, yo=yo: hr.rotate_fuse_weight_out(wo, 0, out=yo),
+            parts[name] = dict(x=wo, fn=lambda wo=wo, yo=yo: hr.rotate_fuse_weight_out(wo, 0, out=yo),
                                bytes=wo.numel() * 4, rows=wo.shape[0])
     if want("r4") or want("r4_kron"):
         w = W["r4"]
@@ -177,7 +183,7 @@ def build_parts(hr, synth, torch, only):
         b = x.numel() * 2 + qbytes(x.shape[0], w.n, spec)
         if want("r4"):
             out = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts["r4"] = dict(fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 2048, spec, out=out),
+            parts["r4"] = dict(x=xg, fn=lambda xg=xg, out=out, spec=spec: hr.rotate_quantize_act(xg, 2048, spec, out=out),
                                bytes=b, rows=x.shape[0])
             host["r4"] = (x, w.n, 2048, [spec], False)
         if want("r4_kron"):
@@ -185,7 +191,7 @@ def build_parts(hr, synth, torch, only):
             # could still hit the 256 MB Infinity Cache
             xk = xg.clone()
             out2 = hr.alloc_quant_outputs(x.shape[0], w.n, spec, dev)
-            parts["r4_kron"] = dict(fn=lambda xk=xk, out=out2, spec=spec: hr.rotate_quantize_act(xk, 0, spec, out=out2),
+            parts["r4_kron"] = dict(x=xk, fn=lambda xk=xk, out=out2, spec=spec: hr.rotate_quantize_act(xk, 0, spec, out=out2),
                                     bytes=b, rows=x.shape[0])
             host["r4_kron"] = (x, w.n, 0, [spec], False)
     if want("r3_q") or want("r3_k"):
@@ -196,12 +202,12 @@ def build_parts(hr, synth, torch, only):
         if want("r3_q"):
             qg = q.to(dev)
             yq = torch.empty_like(qg)
-            parts["r3_q"] = dict(fn=lambda qg=qg, yq=yq: hr.rotate(qg, 0, out=yq), bytes=q.numel() * 4, rows=rows)
+            parts["r3_q"] = dict(x=qg, fn=lambda qg=qg, yq=yq: hr.rotate(qg, 0, out=yq), bytes=q.numel() * 4, rows=rows)
             host["r3_q"] = (q.reshape(rows, 128), 128, 0, [], True)
         if want("r3_k"):
             kg = k.to(dev)
             out = hr.alloc_quant_outputs(rows, 128, spec, dev)
-            parts["r3_k"] = dict(fn=lambda kg=kg, out=out, spec=spec: hr.rotate_quantize_act(kg, 0, spec, out=out),
+            parts["r3_k"] = dict(x=kg, fn=lambda kg=kg, out=out, spec=spec: hr.rotate_quantize_act(kg, 0, spec, out=out),
                                  bytes=k.numel() * 2 + qbytes(rows, 128, spec), rows=rows)
             host["r3_k"] = (k.reshape(rows, 128), 128, 0, [spec], False)
         del q, k
@@ -212,7 +218,7 @@ def build_parts(hr, synth, torch, only):
         xg = x.to(dev)
         rows = x.shape[0]
         out = {"w_rot": torch.empty_like(xg), "quant": [hr.alloc_quant_outputs(rows, w.n, s, dev) for s in specs]}
-        parts["weight"] = dict(fn=lambda xg=xg, out=out, specs=specs: hr.rotate_fuse_weight(xg, 0, specs, out=out),
+        parts["weight"] = dict(x=xg, fn=lambda xg=xg, out=out, specs=specs: hr.rotate_fuse_weight(xg, 0, specs, out=out),
                                bytes=x.numel() * 4 + sum(qbytes(rows, w.n, s) for s in specs), rows=rows)
         host["weight"] = (x, w.n, 0, specs, True)
     return parts, host
@@ -280,6 +286,54 @@ def time_tiny(hr, synth, torch, stream, launches):
     return {"ms_median": round(med, 5), "ms_min": round(ms[0], 5), "bytes": nbytes,
             "GB_s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
             "rows_per_s": round(x.shape[0] / (med * 1e-3), 1), "latency_bound": True}
+
+
+def time_back_to_back(torch, stream, part, launches):
+    """Average duration of one part's launches run back to back, each on the
+    next of n copies of its input (n copies span at least CYCLE_BYTES, 2.5
+    times the 256 MB Infinity Cache, so no launch finds its input there): one
+    event pair around at least `launches` launches (k, after n untimed
+    ones).  Returns (ms, n, k)."""
+    x = part["x"]
+    nbytes = x.numel() * x.element_size()
+    n = max(1, -(-CYCLE_BYTES // nbytes))
+    xs = [x] + [x.clone() for _ in range(n - 1)]
+    k = -(-max(launches, 2 * n) // n) * n
+    for i in range(n):
+        part["fn"](xs[i])
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(k):
+        part["fn"](xs[i % n])
+    b.record(stream)
+    torch.cuda.synchronize()
+    del xs
+    return a.elapsed_time(b) / k, n, k
+
+
+def copy_reference(torch, stream, pairs=3, launches=12):
+    """The runtime's device copy (torch's copy_, a device-to-device memcpy)
+    of 256 MiB into 256 MiB, back to back over `pairs` buffer pairs, timed
+    like the parts: a reference point for a plain read + write stream (it is
+    not a ceiling: the parts that stream whole lines run faster)."""
+    bufs = [(torch.full((COPY_BYTES,), 1, dtype=torch.uint8, device="cuda"),
+             torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")) for _ in range(pairs)]
+    for src, dst in bufs:
+        dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(launches):
+        src, dst = bufs[i % pairs]
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / launches
+    del bufs
+    gbs = 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "bytes": 2 * COPY_BYTES, "GB_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kind": "torch copy_, 256 MiB -> 256 MiB, back to back over %d buffer pairs" % pairs}
 
 
 def traffic_for(kernel: str, digest: str):
@@ -359,9 +413,12 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    # per-launch durations (parts, roofline): K more steps with an event pair
-    # around every launch, on the stream the kernels run on (the events add a
-    # few microseconds per launch, so they stay out of the timed region)
+    # per-launch durations (parts, roofline): each part alone, K launches back
+    # to back over copies of its input, one event pair around them all
+    b2b = {nm: time_back_to_back(torch, stream, parts[nm], args.steps) for nm in names}
+    # and single launches inside K more steps, an event pair around each (the
+    # events add a few microseconds per launch, so they stay out of the timed
+    # region)
     ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] for nm in names}
     for s in range(args.steps):
@@ -372,8 +429,10 @@ def main():
             b.record(stream)
     torch.cuda.synchronize()
     tiny = None
+    copy_ref = None
     if only is None:
         tiny = time_tiny(hr, synth, torch, stream, max(args.steps, 20))
+        copy_ref = copy_reference(torch, stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -387,10 +446,13 @@ def main():
     step_rows = sum(parts[nm]["rows"] for nm in names)
     per = {}
     for nm in names:
-        ms = sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps
+        ms, copies, launches = b2b[nm]
+        ms_single = sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps
         gbs = parts[nm]["bytes"] / (ms * 1e-3) / 1e9
         per[nm] = {"ms": round(ms, 5), "bytes": parts[nm]["bytes"], "GB_s": round(gbs, 1),
-                   "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_per_s": round(parts[nm]["rows"] / (ms * 1e-3), 1)}
+                   "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_per_s": round(parts[nm]["rows"] / (ms * 1e-3), 1),
+                   "input_copies": copies, "launches": launches, "ms_single": round(ms_single, 5),
+                   "frac_single": round(parts[nm]["bytes"] / (ms_single * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     dom = max(names, key=lambda nm: per[nm]["ms"])
     digest = sources_digest()
     roofline = {"bound": "hbm", "kernel": dom, "achieved": per[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -406,7 +468,7 @@ def main():
         "config": {"workload": "hot-path step: " + " + ".join(names), "bytes_per_step": step_bytes,
                    "rows_per_step": step_rows, "io": "bf16 in; int4/MXFP4 codes, bf16 scales/outputs",
                    "parts": per, "sum_of_parts_ms": round(sum(per[nm]["ms"] for nm in names), 5),
-                   "tiny": tiny},
+                   "tiny": tiny, "copy_reference": copy_ref},
         "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -29,8 +29,11 @@
         wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.
 
 Launches are matched to bench.py's parts by order: the bench JSON line gives
-the parts, the steps and the warm-up steps run; each step launches every part
-once (warm-up, timed steps, event pass).
+the parts, the steps and the warm-up steps run.  bench.py launches the
+warm-up steps and the timed steps (every part once per step), then each part
+alone back to back (input_copies untimed launches, then `launches` timed
+ones), then the event pass (every part once per step).  Kernels of the
+runtime and of torch (clones, copies, fills) are skipped.
 """
 import csv
 import hashlib
@@ -39,37 +42,53 @@ import os
 import statistics
 import sys
 
+
+def lib_rows(rows, name_of):
+    return [r for r in rows if not name_of(r).startswith(("__amd", "void at::"))]
+
+
+def phase_of(d):
+    """Phase and part of each library launch, in launch order:
+    [(phase, part)] with phase warm / step / b2b / event."""
+    names = list(d["config"]["parts"].keys())
+    steps, warm = d["steps"], d["warmup_steps_run"]
+    seq = [("warm", n) for _ in range(warm) for n in names]
+    seq += [("step", n) for _ in range(steps) for n in names]
+    for n in names:
+        p = d["config"]["parts"][n]
+        seq += [("b2b_warm", n)] * p.get("input_copies", 0) + [("b2b", n)] * p.get("launches", 0)
+    seq += [("event", n) for _ in range(steps) for n in names]
+    return seq
+
 def cmd_trace(argv):
     trace, bench = argv[0], argv[1]
     d = json.loads(open(bench).read().strip().splitlines()[-1])
     names = list(d["config"]["parts"].keys())
-    steps, warm = d["steps"], d["warmup_steps_run"]
-    rows = [r for r in csv.DictReader(open(trace)) if not r["Kernel_Name"].startswith(("__amd", "void at::"))]
+    rows = lib_rows(list(csv.DictReader(open(trace))), lambda r: r["Kernel_Name"])
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    hot = rows[: (warm + 2 * steps) * len(names)]
-    per = {n: {"step": [], "event": [], "kernel": ""} for n in names}
-    for i, r in enumerate(hot):
-        step, k = divmod(i, len(names))
-        phase = "warm" if step < warm else ("step" if step < warm + steps else "event")
-        if phase == "warm":
-            continue
-        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-        per[names[k]][phase].append(dur)
-        per[names[k]]["kernel"] = r["Kernel_Name"]
-    print("%-8s %6s %12s %12s %10s %10s  %s" % ("part", "calls", "step_avg_us", "event_avg_us", "event_min", "event_max",
-                                                "kernel"))
+    seq = phase_of(d)
+    per = {n: {"step": [], "b2b": [], "event": [], "kernel": ""} for n in names}
+    for (phase, n), r in zip(seq, rows):
+        if phase in per[n]:
+            per[n][phase].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+            per[n]["kernel"] = r["Kernel_Name"]
+    print("%-8s %6s %12s %12s %12s %10s  %s" % ("part", "calls", "step_avg_us", "alone_avg_us", "event_avg_us",
+                                                "alone_min", "kernel"))
     for n in names:
         p = per[n]
-        ev = p["event"]
-        print("%-8s %6d %12.2f %12.2f %10.2f %10.2f  %s" % (n, len(p["step"]) + len(ev), statistics.mean(p["step"]),
-                                                            statistics.mean(ev), min(ev), max(ev), p["kernel"][:110]))
-    tail = rows[(warm + 2 * steps) * len(names):]
+        print("%-8s %6d %12.2f %12.2f %12.2f %10.2f  %s" % (
+            n, len(p["step"]) + len(p["b2b"]) + len(p["event"]), statistics.mean(p["step"]), statistics.mean(p["b2b"]),
+            statistics.mean(p["event"]), min(p["b2b"]), p["kernel"][:110]))
+    tail = rows[len(seq):]
     if tail:
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in tail]
-        print("tiny     %6d %12s %12.2f %10.2f %10.2f  %s" % (len(durs), "-", statistics.median(durs), min(durs),
-                                                               max(durs), tail[0]["Kernel_Name"][:110]))
-    print("bench: value %.1f GB/s, ms_per_step %.5f, sum of event-timed parts %.5f ms, warm-up %d steps in %.2f s"
-          % (d["value"], d["ms_per_step"], d["config"]["sum_of_parts_ms"], warm, d["warmup_s"]))
+        print("tiny     %6d %12s %12.2f %12s %10.2f  %s" % (len(durs), "-", statistics.median(durs), "-", min(durs),
+                                                           tail[0]["Kernel_Name"][:110]))
+    print("bench: value %.1f GB/s, ms_per_step %.5f, sum of parts (alone, back to back) %.5f ms, warm-up %d steps "
+          "in %.2f s" % (d["value"], d["ms_per_step"], d["config"]["sum_of_parts_ms"], d["warmup_steps_run"],
+                         d["warmup_s"]))
+    print("bench per part (us): " + ", ".join("%s %.2f alone / %.2f single" % (
+        n, 1e3 * d["config"]["parts"][n]["ms"], 1e3 * d["config"]["parts"][n]["ms_single"]) for n in names))
 
 
 COPY_KIB = 256 * 1024
@@ -96,14 +115,17 @@ def per_dispatch(path, counter):
     return [(names[k], vals[k]) for k in sorted(vals)]
 
 
-def split(disp, names, warm, steps):
-    hot = [d for d in disp if not d[0].startswith(("__amd", "void at::"))]
-    copies = [v for n, v in disp if n.startswith("__amd_rocclr_copyBuffer")]
+def split(disp, d):
+    """Per-part counter values of the timed steps and the event pass, and
+    the values of the last three runtime copies (bench.py's
+    --copy-calibration: 256 MiB each, after every other launch)."""
+    names = list(d["config"]["parts"].keys())
+    hot = [x for x in disp if not x[0].startswith(("__amd", "void at::"))]
+    copies = [v for n, v in disp if n.startswith("__amd_rocclr_copyBuffer")][-3:]
     out = {n: [] for n in names}
-    for i, (kn, v) in enumerate(hot[: (warm + 2 * steps) * len(names)]):
-        step, k = divmod(i, len(names))
-        if step >= warm:
-            out[names[k]].append(v)
+    for (phase, n), (kn, v) in zip(phase_of(d), hot):
+        if phase in ("step", "event"):
+            out[n].append(v)
     return out, copies
 
 
@@ -112,9 +134,8 @@ def cmd_traffic(argv):
     out_json = argv[4] if len(argv) > 4 else None
     d = json.loads(open(bench).read().strip().splitlines()[-1])
     names = list(d["config"]["parts"].keys())
-    steps, warm = d["steps"], d["warmup_steps_run"]
-    fr, fc = split(per_dispatch(fetch, "FETCH_SIZE"), names, warm, steps)
-    wr, wc = split(per_dispatch(write, "WRITE_SIZE"), names, warm, steps)
+    fr, fc = split(per_dispatch(fetch, "FETCH_SIZE"), d)
+    wr, wc = split(per_dispatch(write, "WRITE_SIZE"), d)
     rf = COPY_KIB / statistics.median(fc)
     wf = COPY_KIB / statistics.median(wc)
     root = os.path.dirname(os.path.abspath(__file__))
@@ -147,7 +168,6 @@ def per_part_counters(path, bench):
     steps and event pass; warm-up dispatches dropped): {part: [dict]}."""
     d = json.loads(open(bench).read().strip().splitlines()[-1])
     names = list(d["config"]["parts"].keys())
-    steps, warm = d["steps"], d["warmup_steps_run"]
     disp = {}
     kname = {}
     for r in csv.DictReader(open(path)):
@@ -157,10 +177,9 @@ def per_part_counters(path, bench):
         kname[k] = r["Kernel_Name"]
     order = [k for k in sorted(disp) if not kname[k].startswith(("__amd", "void at::"))]
     per = {n: [] for n in names}
-    for i, k in enumerate(order[: (warm + 2 * steps) * len(names)]):
-        step, j = divmod(i, len(names))
-        if step >= warm:
-            per[names[j]].append(disp[k])
+    for (phase, n), k in zip(phase_of(d), order):
+        if phase in ("step", "event"):
+            per[n].append(disp[k])
     return per
 
 
