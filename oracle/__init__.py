@@ -13,14 +13,18 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  It shares no code with the HIP library and
 never imports it; the product path must not route through it.
 
-Parity status of each function is stated in its docstring.  One part is
-*parity unpinned* against the pages: the Paley base matrices used for widths
-that are not a power of two are this project's own construction (the pages'
-table of known matrices is not available); they are pinned to the
-mathematics (H_K . H_K^T = K I), not to the pages' matrices.  NVFP4 is
-named on the pages without its encoding: its reading (module text of
-``quant``) is pinned to the public format through PyTorch's float8_e4m3fn
-conversion and to hand-derived cases, not to the pages.
+Parity status of each function is stated in its docstring.  Two choices
+are readings where the pages leave the matter open, each pinned to what the
+mathematics and the public formats fix.  The Paley base matrices used for
+widths that are not a power of two are this project's own construction,
+because the pages' table of known matrices is not available.  They are
+pinned to H_K . H_K^T = K I with +-1 entries, and to the Paley closed form
+(bordered circulant of the quadratic character for prime K - 1).  Another
+Hadamard matrix of the same order would be an equally valid rotation with
+different outputs.  NVFP4 is named on the pages without its encoding.  Its
+reading (module text of ``quant``) is pinned to the public format through
+PyTorch's float8_e4m3fn conversion, E4M3 closed forms and hand-derived
+cases.
 """
 from .hadamard import (  # noqa: F401
     kron_factor,

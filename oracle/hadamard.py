@@ -27,8 +27,9 @@ Readings taken where the pages are silent:
   basis) modulo the first monic irreducible polynomial of degree r when
   monic polynomials are enumerated by the integer a0 + a1 p + ... + a_{r-1}
   p^{r-1}; Q[i][j] = chi(x_i - x_j) (quadratic character);
-  H = I + [[0, 1^T], [-1, Q]].  This base matrix is parity unpinned against
-  the pages' table (not available); it is pinned to H H^T = K I.
+  H = I + [[0, 1^T], [-1, Q]].  The pages' table of known matrices is not
+  available, so which Hadamard matrix of order K is used is a reading; the
+  construction is pinned to H H^T = K I and to its closed form for prime q.
 """
 from __future__ import annotations
 
@@ -152,8 +153,9 @@ def _quadratic_character(q: int):
 def paley_hadamard(k: int) -> np.ndarray:
     """Paley I Hadamard matrix of order k = q + 1 with q a prime power and
     q = 3 (mod 4), as int64 entries +-1 (base matrix for the Kronecker driver,
-    AutoRound "Rotation Transform", section 1.5; the construction itself is
-    parity unpinned against the pages' table, which is not available)."""
+    AutoRound "Rotation Transform", section 1.5; the pages' table is not
+    available, so the choice of this matrix is a reading; pinned to
+    H H^T = k I and, for prime q, to the bordered-circulant closed form)."""
     q = k - 1
     if _prime_power(q) is None or q % 4 != 3:
         raise ValueError("no Paley I construction for order %d" % k)

@@ -137,6 +137,27 @@ def test_paley_hadamard(k):
     assert np.array_equal(h @ h.T, k * np.eye(k, dtype=np.int64))
 
 
+@pytest.mark.parametrize("k", [12, 20, 24, 44, 48, 60, 68, 72, 80, 84, 104, 108, 132, 140])
+def test_paley_prime_closed_form(k):
+    """For prime q = k - 1 the Paley I matrix of AutoRound "Rotation
+    Transform", section 1.5's base orders has the textbook closed form:
+    row 0 all +1, column 0 -1 below it, +1 on the diagonal, and
+    H[1 + a][1 + b] = Legendre(a - b | q) elsewhere.  The Legendre symbol is
+    taken from Euler's criterion (a^((q-1)/2) mod q), not from the oracle's
+    table of squares."""
+    q = k - 1
+    if any(q % d == 0 for d in range(2, int(q ** 0.5) + 1)):
+        pytest.skip("q = %d is not prime" % q)
+    want = np.ones((k, k), dtype=np.int64)
+    want[1:, 0] = -1
+    for a in range(q):
+        for b in range(q):
+            if a != b:
+                e = pow((a - b) % q, (q - 1) // 2, q)
+                want[1 + a, 1 + b] = 1 if e == 1 else -1
+    assert np.array_equal(H.paley_hadamard(k), want)
+
+
 def test_gf27_modulus_and_squares():
     # x^3 + 2x + 1 is the first monic irreducible cubic over GF(3) in the
     # enumeration order (worked by hand: codes 0..6 all have a root in GF(3)).
