@@ -38,7 +38,12 @@ bytes (one read of each input plus every mandatory output write) per second
 over K whole steps with no event between launches.  The per-part durations
 (and the roofline) time each part alone: at least K launches back to back,
 each on the next of n copies of the part's input (n copies span at least
-640 MiB), one event pair around them all.  Each part's single-launch time
+640 MiB), one event pair around them all.  The same is timed for a plain
+streaming kernel (libhrstream.so: 16-byte streaming loads and stores, no
+arithmetic) that reads the part's input from the same copies and writes the
+rest of its algorithmic bytes: stream_floor_ms is what a launch of that shape
+takes here with no computation, and of_stream_floor = stream_floor_ms / ms.
+Each part's single-launch time
 inside K more steps, an event pair around every launch, is reported too
 (ms_single: it adds the events' few microseconds, which matter for the 42 MB
 R1 launch).  copy_reference times the runtime's 256 MiB device copy the same
@@ -288,12 +293,27 @@ def time_tiny(hr, synth, torch, stream, launches):
             "rows_per_s": round(x.shape[0] / (med * 1e-3), 1), "latency_bound": True}
 
 
-def time_back_to_back(torch, stream, part, launches):
+def stream_lib():
+    """ctypes handle of libhrstream.so (the streaming reference), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "hadamard_rotation_preprocessing_amd", "lib", "libhrstream.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hr_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.hr_stream_ref.restype = ctypes.c_int
+    return lib
+
+
+def time_back_to_back(torch, stream, part, launches, sref=None):
     """Average duration of one part's launches run back to back, each on the
     next of n copies of its input (n copies span at least CYCLE_BYTES, 2.5
     times the 256 MB Infinity Cache, so no launch finds its input there): one
     event pair around at least `launches` launches (k, after n untimed
-    ones).  Returns (ms, n, k)."""
+    ones).  With sref (the streaming reference library), the same is timed
+    for a plain streaming kernel that reads the part's input bytes from the
+    same copies and writes the rest of its algorithmic bytes: the floor of
+    that shape.  Returns (ms, n, k, floor_ms or None)."""
     x = part["x"]
     nbytes = x.numel() * x.element_size()
     n = max(1, -(-CYCLE_BYTES // nbytes))
@@ -308,8 +328,27 @@ def time_back_to_back(torch, stream, part, launches):
         part["fn"](xs[i % n])
     b.record(stream)
     torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / k
+    floor_ms = None
+    if sref is not None:
+        wbytes = (part["bytes"] - nbytes) // 16 * 16
+        dst = torch.empty(max(wbytes, 16), dtype=torch.uint8, device=x.device)
+        sp = stream.cuda_stream
+
+        def ref(i):
+            if sref.hr_stream_ref(xs[i].data_ptr(), nbytes // 16 * 16, dst.data_ptr(), wbytes, sp) != 0:
+                raise RuntimeError("streaming reference launch failed")
+        for i in range(n):
+            ref(i)
+        a.record(stream)
+        for i in range(k):
+            ref(i % n)
+        b.record(stream)
+        torch.cuda.synchronize()
+        floor_ms = a.elapsed_time(b) / k
+        del dst
     del xs
-    return a.elapsed_time(b) / k, n, k
+    return ms, n, k, floor_ms
 
 
 def copy_reference(torch, stream, pairs=3, launches=12):
@@ -415,7 +454,8 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     # per-launch durations (parts, roofline): each part alone, K launches back
     # to back over copies of its input, one event pair around them all
-    b2b = {nm: time_back_to_back(torch, stream, parts[nm], args.steps) for nm in names}
+    sref = stream_lib()
+    b2b = {nm: time_back_to_back(torch, stream, parts[nm], args.steps, sref) for nm in names}
     # and single launches inside K more steps, an event pair around each (the
     # events add a few microseconds per launch, so they stay out of the timed
     # region)
@@ -446,13 +486,17 @@ def main():
     step_rows = sum(parts[nm]["rows"] for nm in names)
     per = {}
     for nm in names:
-        ms, copies, launches = b2b[nm]
+        ms, copies, launches, floor_ms = b2b[nm]
         ms_single = sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps
         gbs = parts[nm]["bytes"] / (ms * 1e-3) / 1e9
         per[nm] = {"ms": round(ms, 5), "bytes": parts[nm]["bytes"], "GB_s": round(gbs, 1),
                    "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_per_s": round(parts[nm]["rows"] / (ms * 1e-3), 1),
                    "input_copies": copies, "launches": launches, "ms_single": round(ms_single, 5),
                    "frac_single": round(parts[nm]["bytes"] / (ms_single * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if floor_ms is not None:
+            per[nm]["stream_floor_ms"] = round(floor_ms, 5)
+            per[nm]["stream_floor_frac"] = round(parts[nm]["bytes"] / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            per[nm]["of_stream_floor"] = round(floor_ms / ms, 4)
     dom = max(names, key=lambda nm: per[nm]["ms"])
     digest = sources_digest()
     roofline = {"bound": "hbm", "kernel": dom, "achieved": per[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -32,8 +32,9 @@ Launches are matched to bench.py's parts by order: the bench JSON line gives
 the parts, the steps and the warm-up steps run.  bench.py launches the
 warm-up steps and the timed steps (every part once per step), then each part
 alone back to back (input_copies untimed launches, then `launches` timed
-ones), then the event pass (every part once per step).  Kernels of the
-runtime and of torch (clones, copies, fills) are skipped.
+ones, and the streaming reference for its shape), then the event pass
+(every part once per step).  Kernels of the runtime, of torch (clones,
+copies, fills) and the streaming reference are skipped.
 """
 import csv
 import hashlib
@@ -43,8 +44,14 @@ import statistics
 import sys
 
 
+def is_lib(name):
+    """A launch of the rotate + quantize library (not the runtime's copies,
+    torch's kernels or bench.py's streaming reference)."""
+    return not name.startswith(("__amd", "void at::")) and "stream_kernel" not in name
+
+
 def lib_rows(rows, name_of):
-    return [r for r in rows if not name_of(r).startswith(("__amd", "void at::"))]
+    return [r for r in rows if is_lib(name_of(r))]
 
 
 def phase_of(d):
@@ -120,7 +127,7 @@ def split(disp, d):
     the values of the last three runtime copies (bench.py's
     --copy-calibration: 256 MiB each, after every other launch)."""
     names = list(d["config"]["parts"].keys())
-    hot = [x for x in disp if not x[0].startswith(("__amd", "void at::"))]
+    hot = [x for x in disp if is_lib(x[0])]
     copies = [v for n, v in disp if n.startswith("__amd_rocclr_copyBuffer")][-3:]
     out = {n: [] for n in names}
     for (phase, n), (kn, v) in zip(phase_of(d), hot):
@@ -175,7 +182,7 @@ def per_part_counters(path, bench):
         disp.setdefault(k, {})
         disp[k][r["Counter_Name"]] = disp[k].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         kname[k] = r["Kernel_Name"]
-    order = [k for k in sorted(disp) if not kname[k].startswith(("__amd", "void at::"))]
+    order = [k for k in sorted(disp) if is_lib(kname[k])]
     per = {n: [] for n in names}
     for (phase, n), k in zip(phase_of(d), order):
         if phase in ("step", "event"):

@@ -1,7 +1,9 @@
 """Build step: compiles the HIP library libhadarot.so for gfx950 with hipcc.
 
 Usage: ``python -m hadamard_rotation_preprocessing_amd.build`` (or
-``__graft_entry__.build()``).  Output: ``hadamard_rotation_preprocessing_amd/lib/libhadarot.so``.
+``__graft_entry__.build()``).  Output: ``hadamard_rotation_preprocessing_amd/lib/libhadarot.so``,
+and ``lib/libhrstream.so``, the plain streaming kernel bench.py times as a
+reference (csrc/stream_ref.hip; not part of the rotate + quantize path).
 """
 from __future__ import annotations
 
@@ -16,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libhadarot.so")
+STREAM_LIB = os.path.join(LIBDIR, "libhrstream.so")   # bench.py's streaming reference
 
 ARCH = os.environ.get("HADAROT_ARCH", "gfx950")
 
@@ -69,6 +72,11 @@ def build(verbose: bool = True) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
+    # bench.py's streaming reference (a separate library: not part of the path)
+    tmp = STREAM_LIB + ".tmp"
+    _run([hipcc, "-shared", "-x", "hip", os.path.join(CSRC, "stream_ref.hip"), "-o", tmp] + COMMON +
+         ["--offload-arch=" + ARCH] + DEVICE_FLAGS, verbose)
+    os.replace(tmp, STREAM_LIB)
     return LIB
 
 

@@ -765,136 +765,157 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 // q = l >> 4; chunk c in {0, 1} holds row elements 64 c + 32 h + 8 q + r.
 // The MFMA (16x16x32, one 16-byte load as B) transforms bits {0..4},
 // registers bit 6, the DPP butterfly bit 5.  The 128 elements of a row sit in the 8 lanes sharing n >> 1.
+// Groups of eight 128-element rows per k128 wave.  The quantising instances
+// load two groups up front (twice the bytes in flight per wave, the set-up
+// shared): the R3 key kernel measured 60.5 -> 58.9 us with two, 60.3 with four
+// (79 VGPRs, six waves per SIMD) and 63.5 with eight.  The plain rotation
+// keeps one, which measured faster there.
+template <class Q0>
+__host__ __device__ constexpr int k128_groups() {
+    return Q0::fmt == 0 ? 2 : 1;
+}
+
 template <bool WROT, class Q0>
 __global__ void __launch_bounds__(256) k128(const FastArgs a) {
+    constexpr int G = k128_groups<Q0>();   // groups of eight rows per wave
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int n = lane & 15;
     const int h = n & 1;
     const int qq = lane >> 4;
-    const int64_t row = (static_cast<int64_t>(blockIdx.x) * 4 + wv) * 8 + (n >> 1);
-    const bool valid = row < a.units;
+    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + wv) * 8 * G + (n >> 1);
     const int col0 = 32 * h + 8 * qq;  // element of chunk 0 within the row
-    // rows past the end re-read the last row (finite data, never stored)
-    const int64_t lrow = valid ? row : a.units - 1;
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + lrow * 128 + col0;
-    u32x4_t raw[2];
+    // every group's loads first; rows past the end re-read the last row
+    // (finite data, never stored)
+    u32x4_t raws[G][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) raw[c] = ldg16(src + 64 * c);
+    for (int gi = 0; gi < G; ++gi) {
+        const int64_t row = row0 + 8 * gi;
+        const int64_t lrow = row < a.units ? row : a.units - 1;
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + lrow * 128 + col0;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) raws[gi][c] = ldg16(src + 64 * c);
+    }
     const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(&kH32.w[0][lane][0]);   // hp[64]: row half 1
     const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, hp[0]);
     const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, hp[64]);
-    float v[16];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const bf16x8_t Bc = __builtin_bit_cast(bf16x8_t, raw[c]);
-        const f32x4v_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Bc, f32x4v_t{}, 0, 0, 0);
-        const f32x4v_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bc, f32x4v_t{}, 0, 0, 0);
+    for (int gi = 0; gi < G; ++gi) {
+        const int64_t row = row0 + 8 * gi;
+        const bool valid = row < a.units;
+        const u32x4_t (&raw)[2] = raws[gi];
+        float v[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[8 * c + j] = d0[j];
-            v[8 * c + 4 + j] = d1[j];
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8_t Bc = __builtin_bit_cast(bf16x8_t, raw[c]);
+            const f32x4v_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Bc, f32x4v_t{}, 0, 0, 0);
+            const f32x4v_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bc, f32x4v_t{}, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * c + j] = d0[j];
+                v[8 * c + 4 + j] = d1[j];
+            }
         }
-    }
-    bfly<16, 0x8u>(v);                           // bit 6 (v-index bit 3)
-    dpp_bfly<kXor1>(v, h ? -1.0f : 1.0f);        // bit 5
-    const int64_t e0 = row * 128 + col0;
+        bfly<16, 0x8u>(v);                           // bit 6 (v-index bit 3)
+        dpp_bfly<kXor1>(v, h ? -1.0f : 1.0f);        // bit 5
+        const int64_t e0 = row * 128 + col0;
 
-    if constexpr (WROT) {
-        uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
-        float y[16];
+        if constexpr (WROT) {
+            uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
+            float y[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) y[j] = v[j] * a.norm;
-        if (valid) {
+            for (int j = 0; j < 16; ++j) y[j] = v[j] * a.norm;
+            if (valid) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-                stg16(dst + 64 * c, u32x4_t{bf16x2(y[8 * c], y[8 * c + 1]), bf16x2(y[8 * c + 2], y[8 * c + 3]),
-                                            bf16x2(y[8 * c + 4], y[8 * c + 5]), bf16x2(y[8 * c + 6], y[8 * c + 7])});
-        }
-    }
-    if constexpr (Q0::fmt == 0) {
-        static_assert(Q0::logg == 7, "one group per row");
-        const float f = a.norm;
-        float s, zf = 0.0f;
-        if constexpr (Q0::sym) {
-            float am = fabsf(v[0]);
-#pragma unroll
-            for (int j = 1; j < 16; ++j) am = fmaxf(am, fabsf(v[j]));
-            am = fmaxf(am, dpp<kXor1>(am));
-            am = fmaxf(am, __shfl_xor(am, 16));
-            am = fmaxf(am, __shfl_xor(am, 32));
-            s = (am * f) * (1.0f / 7.0f);
-        } else {
-            float hi = v[0], nl = -v[0];
-#pragma unroll
-            for (int j = 1; j < 16; ++j) {
-                hi = fmaxf(hi, v[j]);
-                nl = fmaxf(nl, -v[j]);
+                for (int c = 0; c < 2; ++c)
+                    stg16(dst + 64 * c, u32x4_t{bf16x2(y[8 * c], y[8 * c + 1]), bf16x2(y[8 * c + 2], y[8 * c + 3]),
+                                                bf16x2(y[8 * c + 4], y[8 * c + 5]), bf16x2(y[8 * c + 6], y[8 * c + 7])});
             }
-            hi = fmaxf(hi, dpp<kXor1>(hi));
-            nl = fmaxf(nl, dpp<kXor1>(nl));
-            hi = fmaxf(hi, __shfl_xor(hi, 16));
-            nl = fmaxf(nl, __shfl_xor(nl, 16));
-            hi = fmaxf(hi, __shfl_xor(hi, 32));
-            nl = fmaxf(nl, __shfl_xor(nl, 32));
-            hi = fmaxf(hi, 0.0f) * f;
-            nl = fmaxf(nl, 0.0f) * f;
-            s = (hi + nl) * (1.0f / 15.0f);
-            zf = nl;
         }
-        uint32_t sbits = 0;
-        if constexpr (Q0::sdt == 1) {
-            sbits = f2bf(s);
-            s = bf2f(sbits);
-            if (s == 0.0f) {
+        if constexpr (Q0::fmt == 0) {
+            static_assert(Q0::logg == 7, "one group per row");
+            const float f = a.norm;
+            float s, zf = 0.0f;
+            if constexpr (Q0::sym) {
+                float am = fabsf(v[0]);
+#pragma unroll
+                for (int j = 1; j < 16; ++j) am = fmaxf(am, fabsf(v[j]));
+                am = fmaxf(am, dpp<kXor1>(am));
+                am = fmaxf(am, __shfl_xor(am, 16));
+                am = fmaxf(am, __shfl_xor(am, 32));
+                s = (am * f) * (1.0f / 7.0f);
+            } else {
+                float hi = v[0], nl = -v[0];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) {
+                    hi = fmaxf(hi, v[j]);
+                    nl = fmaxf(nl, -v[j]);
+                }
+                hi = fmaxf(hi, dpp<kXor1>(hi));
+                nl = fmaxf(nl, dpp<kXor1>(nl));
+                hi = fmaxf(hi, __shfl_xor(hi, 16));
+                nl = fmaxf(nl, __shfl_xor(nl, 16));
+                hi = fmaxf(hi, __shfl_xor(hi, 32));
+                nl = fmaxf(nl, __shfl_xor(nl, 32));
+                hi = fmaxf(hi, 0.0f) * f;
+                nl = fmaxf(nl, 0.0f) * f;
+                s = (hi + nl) * (1.0f / 15.0f);
+                zf = nl;
+            }
+            uint32_t sbits = 0;
+            if constexpr (Q0::sdt == 1) {
+                sbits = f2bf(s);
+                s = bf2f(sbits);
+                if (s == 0.0f) {
+                    s = 1.0f;
+                    sbits = 0x3F80u;
+                }
+            } else if (s == 0.0f) {
                 s = 1.0f;
-                sbits = 0x3F80u;
             }
-        } else if (s == 0.0f) {
-            s = 1.0f;
-        }
-        const float rs = __builtin_amdgcn_rcpf(s);
-        const float inv = f * rs;
-        uint32_t w[2];
-        uint32_t zi = 0;
-        if constexpr (Q0::sym) {
-            const float off = kMagic + 8.0f;
+            const float rs = __builtin_amdgcn_rcpf(s);
+            const float inv = f * rs;
+            uint32_t w[2];
+            uint32_t zi = 0;
+            if constexpr (Q0::sym) {
+                const float off = kMagic + 8.0f;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                float t[8];
+                for (int c = 0; c < 2; ++c) {
+                    float t[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) t[j] = fmaf(v[8 * c + j], inv, off);
-                w[c] = pack8(t) ^ 0x88888888u;
+                    for (int j = 0; j < 8; ++j) t[j] = fmaf(v[8 * c + j], inv, off);
+                    w[c] = pack8(t) ^ 0x88888888u;
+                }
+            } else {
+                const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
+                zi = static_cast<uint32_t>(z);
+                const uint32_t zmul = zi * 0x1111u;
+                const float lo = kMagic - z, hi = kMagic + 15.0f - z;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float t[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(v[8 * c + j], inv, kMagic), lo, hi);
+                    w[c] = pack8z(t, zmul);
+                }
+                // rows 2m, 2m + 1 live in lanes 4m, 4m + 2 (q = 0): one byte
+                const uint32_t zodd = dppu<kXor2>(zi);
+                if (valid && qq == 0 && (n & 3) == 0) {
+                    uint32_t byte = zi & 0xFu;
+                    if (row + 1 < a.units) byte |= (zodd & 0xFu) << 4;
+                    a.q[0].zeros[row >> 1] = static_cast<uint8_t>(byte);
+                }
             }
-        } else {
-            const float z = fminf(fmaxf(rintf(zf * rs), 0.0f), 15.0f);
-            zi = static_cast<uint32_t>(z);
-            const uint32_t zmul = zi * 0x1111u;
-            const float lo = kMagic - z, hi = kMagic + 15.0f - z;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                float t[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(v[8 * c + j], inv, kMagic), lo, hi);
-                w[c] = pack8z(t, zmul);
-            }
-            // rows 2m, 2m + 1 live in lanes 4m, 4m + 2 (q = 0): one byte
-            const uint32_t zodd = dppu<kXor2>(zi);
-            if (valid && qq == 0 && (n & 3) == 0) {
-                uint32_t byte = zi & 0xFu;
-                if (row + 1 < a.units) byte |= (zodd & 0xFu) << 4;
-                a.q[0].zeros[row >> 1] = static_cast<uint8_t>(byte);
-            }
-        }
-        if (valid) {
-            uint32_t* cp = reinterpret_cast<uint32_t*>(a.q[0].codes + (e0 >> 1));
-            cp[0] = w[0];
-            cp[8] = w[1];  // chunk 1 is 64 elements = 32 bytes further
-            if (qq == 0 && h == 0) {
-                if constexpr (Q0::sdt == 1)
-                    static_cast<uint16_t*>(a.q[0].scales)[row] = static_cast<uint16_t>(sbits);
-                else
-                    static_cast<float*>(a.q[0].scales)[row] = s;
+            if (valid) {
+                uint32_t* cp = reinterpret_cast<uint32_t*>(a.q[0].codes + (e0 >> 1));
+                cp[0] = w[0];
+                cp[8] = w[1];  // chunk 1 is 64 elements = 32 bytes further
+                if (qq == 0 && h == 0) {
+                    if constexpr (Q0::sdt == 1)
+                        static_cast<uint16_t*>(a.q[0].scales)[row] = static_cast<uint16_t>(sbits);
+                    else
+                        static_cast<float*>(a.q[0].scales)[row] = s;
+                }
             }
         }
     }
@@ -1548,7 +1569,8 @@ int try_kwave(const FastKey& k, const FastArgs& a, hipStream_t s) {
 template <bool WROT, class Q0>
 int try_k128(const FastKey& k, const FastArgs& a, hipStream_t s) {
     if (k.mixed || k.logb != 7 || k.wrot != (WROT ? 1 : 0) || !qmatch<Q0>(k, 0) || k.nq > 1) return 0;
-    const int64_t grid = (a.units + 31) / 32;
+    constexpr int64_t rows_per_block = 32 * k128_groups<Q0>();
+    const int64_t grid = (a.units + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL((k128<WROT, Q0>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 1 : -static_cast<int>(e);
