@@ -47,7 +47,10 @@ Each part's single-launch time
 inside K more steps, an event pair around every launch, is reported too
 (ms_single: it adds the events' few microseconds, which matter for the 42 MB
 R1 launch).  copy_reference times the runtime's 256 MiB device copy the same
-way, as a reference point.  Prints one JSON line.
+way, as a reference point.  valu_clock_mhz is the shader clock measured
+right before and right after the timed steps (an FMA issue-rate probe in
+libhrstream.so): boxes of this model run at different clocks, which moves the
+parts that are bound by their instruction stream.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -302,7 +305,35 @@ def stream_lib():
     lib = ctypes.CDLL(path)
     lib.hr_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.hr_stream_ref.restype = ctypes.c_int
+    lib.hr_clock_ref.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hr_clock_ref.restype = ctypes.c_int
     return lib
+
+
+def valu_clock_mhz(torch, stream, sref, iters=20000):
+    """Shader clock from libhrstream's FMA issue probe: four waves per SIMD,
+    each issuing iters * 8 independent wave64 FMAs (4 cycles each), so every
+    SIMD is busy 4 * iters * 8 * 4 cycles.  The GPU's clock under power
+    management differs between boxes, and the parts bound by their
+    instruction stream (r4_kron, and r1, r4 and weight in part) follow it."""
+    if sref is None:
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 4 * cus
+    out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+    for _ in range(2):
+        if sref.hr_clock_ref(out.data_ptr(), blocks, iters // 10, sp) != 0:
+            raise RuntimeError("clock probe launch failed")
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    if sref.hr_clock_ref(out.data_ptr(), blocks, iters, sp) != 0:
+        raise RuntimeError("clock probe launch failed")
+    b.record(stream)
+    torch.cuda.synchronize()
+    cycles = 4 * iters * 8 * 4
+    return round(cycles / (a.elapsed_time(b) * 1e-3) / 1e6, 1)
 
 
 def time_back_to_back(torch, stream, part, launches, sref=None):
@@ -442,6 +473,8 @@ def main():
 
     # the timed region: K whole steps, nothing recorded between launches
     stream = torch.cuda.current_stream()
+    sref = stream_lib()
+    clock_before = valu_clock_mhz(torch, stream, sref)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -454,7 +487,7 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     # per-launch durations (parts, roofline): each part alone, K launches back
     # to back over copies of its input, one event pair around them all
-    sref = stream_lib()
+    clock_after = valu_clock_mhz(torch, stream, sref)
     b2b = {nm: time_back_to_back(torch, stream, parts[nm], args.steps, sref) for nm in names}
     # and single launches inside K more steps, an event pair around each (the
     # events add a few microseconds per launch, so they stay out of the timed
@@ -512,7 +545,8 @@ def main():
         "config": {"workload": "hot-path step: " + " + ".join(names), "bytes_per_step": step_bytes,
                    "rows_per_step": step_rows, "io": "bf16 in; int4/MXFP4 codes, bf16 scales/outputs",
                    "parts": per, "sum_of_parts_ms": round(sum(per[nm]["ms"] for nm in names), 5),
-                   "tiny": tiny, "copy_reference": copy_ref},
+                   "tiny": tiny, "copy_reference": copy_ref,
+                   "valu_clock_mhz": {"before_timed_steps": clock_before, "after_timed_steps": clock_after}},
         "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -46,8 +46,8 @@ import sys
 
 def is_lib(name):
     """A launch of the rotate + quantize library (not the runtime's copies,
-    torch's kernels or bench.py's streaming reference)."""
-    return not name.startswith(("__amd", "void at::")) and "stream_kernel" not in name
+    torch's kernels or bench.py's streaming and clock references)."""
+    return not name.startswith(("__amd", "void at::")) and "stream_kernel" not in name and "clock_kernel" not in name
 
 
 def lib_rows(rows, name_of):

@@ -34,7 +34,35 @@ __global__ void __launch_bounds__(kThreads) stream_kernel(const u32x4_t* __restr
         if (i < nw) __builtin_nontemporal_store(acc ^ v[k], dst + i);
     }
 }
+// Issue-rate probe: every thread runs eight independent float FMA chains
+// for `iters` rounds.  With W waves per SIMD and nothing else running, a
+// SIMD issues a wave64 FMA every 4 cycles, so the launch takes about
+// W * iters * 8 * 4 cycles: its duration gives the shader clock the GPU ran
+// at (it varies between GPUs of one model under power management).
+__global__ void __launch_bounds__(kThreads) clock_kernel(float* out, int iters, float a) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(threadIdx.x) * 1e-3f + static_cast<float>(i);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], a, 0.5f);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+    if (s == 12345.0f) out[blockIdx.x] = s;   // keeps the chains live; practically never stored
+}
 }  // namespace
+
+// Runs clock_kernel on `blocks` workgroups of 256 threads (out: at least
+// `blocks` floats of device memory, practically never written).  Returns 0,
+// -1 for invalid arguments, or -3 if the launch failed.
+extern "C" int hr_clock_ref(float* out, int blocks, int iters, void* stream) {
+    if (out == nullptr || blocks <= 0 || iters <= 0) return -1;
+    hipLaunchKernelGGL(clock_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), out, iters, 0.999f);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 // Reads read_bytes from src and writes write_bytes to dst (both multiples of
 // 16; pointers 16-byte aligned; device memory) in one launch on `stream`.
