@@ -1104,8 +1104,11 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
         zret = zi;
     }
     if (valid) {
-        stg16(cp, u32x4_t{w[0], w[1], w[2], w[3]});
-        stg16(cp + 16, u32x4_t{w[4], w[5], w[6], w[7]});
+        // ordinary stores: the four quarters of a 128-byte line of codes come
+        // from four waves, and the L2 merges them (streaming stores of these
+        // pieces wrote 1.48 times the code bytes to HBM)
+        stg16c(cp, u32x4_t{w[0], w[1], w[2], w[3]});
+        stg16c(cp + 16, u32x4_t{w[4], w[5], w[6], w[7]});
         if (first) static_cast<uint16_t*>(q.scales)[gidx] = static_cast<uint16_t>(sbits);
     }
     return zret;
@@ -1226,7 +1229,7 @@ kkron(const KronArgs a) {
 #pragma unroll
                     for (int p = 0; p < 4; ++p)
                         o[p] = bf16x2(v[kron_elem(m, 2 * p)] * a.norm, v[kron_elem(m, 2 * p + 1)] * a.norm);
-                    stg16(dst + 8 * m, o);
+                    stg16c(dst + 8 * m, o);   // a lane's 8 pieces fill one line: merged in L2
                 }
             }
         }
@@ -1410,7 +1413,7 @@ __global__ void __launch_bounds__(64 * ((K + 31) / 32), 4) kkronw(const KronArgs
 #pragma unroll
                     for (int p = 0; p < 4; ++p)
                         o[p] = bf16x2(v[kron_elem(m, 2 * p)] * a.norm, v[kron_elem(m, 2 * p + 1)] * a.norm);
-                    stg16(dst + 8 * m, o);
+                    stg16c(dst + 8 * m, o);   // a lane's 8 pieces fill one line: merged in L2
                 }
             }
         }
