@@ -130,12 +130,34 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
-// Butterfly across a lane bit: lane with the bit clear gets own + partner,
-// lane with the bit set gets partner - own (sgn = -1 there).
-template <int CTRL, int N>
-__device__ __forceinline__ void dpp_bfly(float (&v)[N], float sgn) {
+// Butterfly across lane bit 0 in one v_fmac_f32_dpp per value: the lane
+// with the bit clear gets own + partner, the lane with the bit set own -
+// partner (sgn = -1 there), which is exactly -(partner - own).  Those lanes
+// therefore hold the negated transform from here on; the caller multiplies
+// by sgn again where it normalises, or passes it on to the epilogue inside
+// the factor f (a negative f).
+// (The compiler does not fold a DPP move into v_fmac_f32, so the stage is
+// written out: eight values per block; the leading s_nop 1 gives the two wait
+// states a DPP read of a VGPR needs after a VALU write of it, and within a
+// block no instruction reads a register another one writes.)
+template <int N>
+__device__ __forceinline__ void dpp_bfly_neg_xor1(float (&v)[N], float sgn) {
+    static_assert(N % 8 == 0, "blocks of eight values");
 #pragma unroll
-    for (int j = 0; j < N; ++j) v[j] = fmaf(sgn, v[j], dpp<CTRL>(v[j]));
+    for (int j = 0; j < N; j += 8) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+            : "+v"(v[j]), "+v"(v[j + 1]), "+v"(v[j + 2]), "+v"(v[j + 3]), "+v"(v[j + 4]), "+v"(v[j + 5]),
+              "+v"(v[j + 6]), "+v"(v[j + 7])
+            : "v"(sgn));
+    }
 }
 
 // Maximum over aligned groups of GL consecutive lanes.
@@ -197,7 +219,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
 #pragma unroll
         for (int j = 1; j < E; ++j) am = fmaxf(am, fabsf(u[j]));
         am = lanes_max<GL>(am);
-        s = (am * f) * (1.0f / 7.0f);
+        s = (am * fabsf(f)) * (1.0f / 7.0f);
     } else {
         float hi = u[0], nl = -u[0];
 #pragma unroll
@@ -205,8 +227,13 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
             hi = fmaxf(hi, u[j]);
             nl = fmaxf(nl, -u[j]);
         }
-        hi = fmaxf(lanes_max<GL>(hi), 0.0f) * f;
-        nl = fmaxf(lanes_max<GL>(nl), 0.0f) * f;  // -min(min y, 0)
+        if (f < 0.0f) {   // the lane holds -y: max y = max(-u), -min y = max u
+            const float t = hi;
+            hi = nl;
+            nl = t;
+        }
+        hi = fmaxf(lanes_max<GL>(hi), 0.0f) * fabsf(f);
+        nl = fmaxf(lanes_max<GL>(nl), 0.0f) * fabsf(f);  // -min(min y, 0)
         s = (hi + nl) * (1.0f / 15.0f);
         zf = nl;
     }
@@ -314,7 +341,7 @@ __device__ __forceinline__ void epi_int_small(const float (&u)[E], float f, cons
             float am = fabsf(v[0]);
 #pragma unroll
             for (int j = 1; j < G; ++j) am = fmaxf(am, fabsf(v[j]));
-            s = (am * f) * (1.0f / 7.0f);
+            s = (am * fabsf(f)) * (1.0f / 7.0f);
         } else {
             float hi = v[0], nl = -v[0];
 #pragma unroll
@@ -322,8 +349,13 @@ __device__ __forceinline__ void epi_int_small(const float (&u)[E], float f, cons
                 hi = fmaxf(hi, v[j]);
                 nl = fmaxf(nl, -v[j]);
             }
-            hi = fmaxf(hi, 0.0f) * f;
-            nl = fmaxf(nl, 0.0f) * f;  // -min(min y, 0)
+            if (f < 0.0f) {   // the lane holds -y
+                const float t = hi;
+                hi = nl;
+                nl = t;
+            }
+            hi = fmaxf(hi, 0.0f) * fabsf(f);
+            nl = fmaxf(nl, 0.0f) * fabsf(f);  // -min(min y, 0)
             s = (hi + nl) * (1.0f / 15.0f);
             zf = nl;
         }
@@ -693,7 +725,10 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         wave_sync();
     }
     bfly<E, 0x38u>(y);                                   // bits 3, 4, 5
-    if constexpr (LOGB >= 7) dpp_bfly<kXor1>(y, (lane & 1) ? -1.0f : 1.0f);   // bit 6
+    // bit 6; odd lanes then hold -y (sig), undone at the normalisation or in
+    // the epilogue's factor
+    const float sig = (LOGB >= 7 && (lane & 1)) ? -1.0f : 1.0f;
+    if constexpr (LOGB >= 7) dpp_bfly_neg_xor1(y, sig);
     if constexpr (PAIR) {
         // bit 12 across the pair: four passes of 16 values per lane through
         // the transpose buffers (value j of lane l at 65 j + l: no bank
@@ -731,10 +766,10 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
         }
     }
     constexpr bool need_y = WROT || Q0::fmt == 1 || Q1::fmt == 1;
-    float f = a.norm;
+    float f = sig * a.norm;   // y = f * (the lane's values)
     if constexpr (need_y) {
 #pragma unroll
-        for (int j = 0; j < E; ++j) y[j] *= a.norm;
+        for (int j = 0; j < E; ++j) y[j] *= f;
         f = 1.0f;
     }
     if constexpr (WROT) {
@@ -817,14 +852,17 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
             }
         }
         bfly<16, 0x8u>(v);                           // bit 6 (v-index bit 3)
-        dpp_bfly<kXor1>(v, h ? -1.0f : 1.0f);        // bit 5
+        // bit 5: odd lanes then hold -y, undone by the signed factor f
+        const float sig = h ? -1.0f : 1.0f;
+        dpp_bfly_neg_xor1(v, sig);
         const int64_t e0 = row * 128 + col0;
 
         if constexpr (WROT) {
             uint16_t* dst = static_cast<uint16_t*>(a.y_rot) + e0;
             float y[16];
+            const float fy = sig * a.norm;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) y[j] = v[j] * a.norm;
+            for (int j = 0; j < 16; ++j) y[j] = v[j] * fy;
             if (valid) {
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
@@ -834,7 +872,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
         }
         if constexpr (Q0::fmt == 0) {
             static_assert(Q0::logg == 7, "one group per row");
-            const float f = a.norm;
+            const float f = a.norm;   // y = sig * f * v
             float s, zf = 0.0f;
             if constexpr (Q0::sym) {
                 float am = fabsf(v[0]);
@@ -850,6 +888,11 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
                 for (int j = 1; j < 16; ++j) {
                     hi = fmaxf(hi, v[j]);
                     nl = fmaxf(nl, -v[j]);
+                }
+                if (h) {   // the lane holds -y: max y = max(-v), -min y = max v
+                    const float t = hi;
+                    hi = nl;
+                    nl = t;
                 }
                 hi = fmaxf(hi, dpp<kXor1>(hi));
                 nl = fmaxf(nl, dpp<kXor1>(nl));
@@ -874,7 +917,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
                 s = 1.0f;
             }
             const float rs = __builtin_amdgcn_rcpf(s);
-            const float inv = f * rs;
+            const float inv = sig * (f * rs);
             uint32_t w[2];
             uint32_t zi = 0;
             if constexpr (Q0::sym) {
