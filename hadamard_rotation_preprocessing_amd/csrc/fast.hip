@@ -804,7 +804,8 @@ __global__ void __launch_bounds__(256) kwave(const FastArgs a) {
 // load two groups up front (twice the bytes in flight per wave, the set-up
 // shared): the R3 key kernel measured 60.5 -> 58.9 us with two, 60.3 with four
 // (79 VGPRs, six waves per SIMD) and 63.5 with eight.  The plain rotation
-// keeps one, which measured faster there.
+// keeps one, which measured faster there.  (Quantising without a rotated
+// output now runs k128q; this applies to the instances that also write y.)
 template <class Q0>
 __host__ __device__ constexpr int k128_groups() {
     return Q0::fmt == 0 ? 2 : 1;

@@ -436,6 +436,14 @@ def test_head_dim_rows_ragged_asym(kernel_path, rows):
         assert int(out["zeros"][-1].item()) >> 4 == 0
 
 
+@pytest.mark.parametrize("rows", [1, 15, 17, 64, 1001])
+def test_head_dim_rows_ragged_sym(kernel_path, rows):
+    # n = 128, one symmetric group per row (the R3 key kernel handles 16 rows
+    # per wave: partial waves at the end)
+    x = synth.gaussian((rows, 128), seed=6000 + rows, dtype=torch.bfloat16)
+    run_act(x, 128, 0, hr.QSpec("int", 4, 128, True, "bf16"))
+
+
 @pytest.mark.parametrize("block", [32, 0])
 def test_mxfp4_activations(kernel_path, block):
     # block-32 rotation with MXFP4 activations (the pages' accuracy setting)
