@@ -137,27 +137,36 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v) {
 // by sgn again where it normalises, or passes it on to the epilogue inside
 // the factor f (a negative f).
 // (The compiler does not fold a DPP move into v_fmac_f32, so the stage is
-// written out: eight values per block; the leading s_nop 1 gives the two wait
-// states a DPP read of a VGPR needs after a VALU write of it, and within a
-// block no instruction reads a register another one writes.)
+// written out, eight values per block.  Its hazard recognizer does not look
+// inside inline asm, so the blocks carry their own wait states: a DPP read of
+// a VGPR needs two after a VALU write of it (s_nop 1 before each block;
+// inside a block no instruction reads a register another one writes), and
+// five after a VALU write of EXEC (s_nop 4 before the first block: EXEC only
+// changes at control flow, and the stage is one unrolled basic block).)
 template <int N>
 __device__ __forceinline__ void dpp_bfly_neg_xor1(float (&v)[N], float sgn) {
     static_assert(N % 8 == 0, "blocks of eight values");
+#define HR_DPP_FMAC8(NOP)                                                                          \
+    asm(NOP "\n\t"                                                                                 \
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"             \
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"                 \
+        : "+v"(v[j]), "+v"(v[j + 1]), "+v"(v[j + 2]), "+v"(v[j + 3]), "+v"(v[j + 4]), "+v"(v[j + 5]), \
+          "+v"(v[j + 6]), "+v"(v[j + 7])                                                           \
+        : "v"(sgn))
 #pragma unroll
     for (int j = 0; j < N; j += 8) {
-        asm("s_nop 1\n\t"
-            "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-            "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-            : "+v"(v[j]), "+v"(v[j + 1]), "+v"(v[j + 2]), "+v"(v[j + 3]), "+v"(v[j + 4]), "+v"(v[j + 5]),
-              "+v"(v[j + 6]), "+v"(v[j + 7])
-            : "v"(sgn));
+        if (j == 0)
+            HR_DPP_FMAC8("s_nop 4");
+        else
+            HR_DPP_FMAC8("s_nop 1");
     }
+#undef HR_DPP_FMAC8
 }
 
 // Maximum over aligned groups of GL consecutive lanes.
