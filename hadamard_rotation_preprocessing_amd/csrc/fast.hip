@@ -196,11 +196,18 @@ __device__ __forceinline__ uint32_t pack8(const float* t) {
 // Below bit 22 the bits of kMagic + c are those of the integer c, so the sum
 // of the four shifted words is exact modulo 2^16; adding zmul once per four
 // elements then gives the nibbles c + z in 0..15, which never carry.
+// (a << 4) + b in one v_lshl_add_u32: the compiler forms separate shifts and
+// v_add3_u32 from the plain expression, five instructions per four codes
+// against four for this Horner chain.
+__device__ __forceinline__ uint32_t shl4_add(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_lshl_add_u32 %0, %1, 4, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
 __device__ __forceinline__ uint32_t pack8z(const float* r, uint32_t zmul) {
-    const uint32_t a0 = __float_as_uint(r[0]) + (__float_as_uint(r[1]) << 4) + (__float_as_uint(r[2]) << 8) +
-                        (__float_as_uint(r[3]) << 12) + zmul;
-    const uint32_t a1 = __float_as_uint(r[4]) + (__float_as_uint(r[5]) << 4) + (__float_as_uint(r[6]) << 8) +
-                        (__float_as_uint(r[7]) << 12) + zmul;
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(r);
+    const uint32_t a0 = shl4_add(shl4_add(shl4_add(b[3], b[2]), b[1]), b[0]) + zmul;
+    const uint32_t a1 = shl4_add(shl4_add(shl4_add(b[7], b[6]), b[5]), b[4]) + zmul;
     return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
 }
 
