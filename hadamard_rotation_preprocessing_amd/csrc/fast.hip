@@ -211,6 +211,40 @@ __device__ __forceinline__ uint32_t pack8z(const float* r, uint32_t zmul) {
     return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
 }
 
+// Asymmetric INT4 codes of NB runs of eight values el(b, j), j < 8:
+// clamp(rne(u inv), lo, hi) in kMagic units (lo = kMagic - z, hi = kMagic +
+// 15 - z), packed by pack8z.  fma(u, inv, kMagic) rounds u inv + kMagic once,
+// which is monotone in u (either direction, by the sign of inv), so when the
+// codes of the lane's largest and smallest u both lie in [lo, hi] so does
+// every code and the clamp is the identity.  A wave whose lanes all pass that
+// test skips the clamp (one v_med3 per value); its codes are bit for bit the
+// clamped ones.  On Gaussian-like rows about one group in a hundred needs the
+// clamp: the bf16 scale can round below (hi - lo) / 15 and the two ends of
+// the range can both round outwards.
+template <int NB, class El>
+__device__ __forceinline__ void codes_asym(El el, float inv, float lo, float hi, uint32_t zmul, float umax,
+                                           float umin, uint32_t* w) {
+    const float c0 = fmaf(umax, inv, kMagic), c1 = fmaf(umin, inv, kMagic);
+    const bool inside = fminf(c0, c1) >= lo && fmaxf(c0, c1) <= hi;
+    if (__builtin_amdgcn_ballot_w64(!inside) == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = fmaf(el(b, j), inv, kMagic);
+            w[b] = pack8z(t, zmul);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(el(b, j), inv, kMagic), lo, hi);
+            w[b] = pack8z(t, zmul);
+        }
+    }
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // Two floats -> two bfloat16 (v_cvt_pk_bf16_f32, round to nearest even).
@@ -230,6 +264,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
     static_assert(G >= E, "group spans whole lanes");
     constexpr int GL = G / E;
     float s, zf = 0.0f;
+    float umax = 0.0f, umin = 0.0f;   // the lane's extremes of u (asymmetric)
     if constexpr (Q::sym) {
         float am = fabsf(u[0]);
 #pragma unroll
@@ -243,6 +278,8 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
             hi = fmaxf(hi, u[j]);
             nl = fmaxf(nl, -u[j]);
         }
+        umax = hi;
+        umin = -nl;
         if (f < 0.0f) {   // the lane holds -y: max y = max(-u), -min y = max u
             const float t = hi;
             hi = nl;
@@ -287,13 +324,7 @@ __device__ __forceinline__ void epi_int(const float (&u)[E], float f, const Quan
         const uint32_t zi = static_cast<uint32_t>(z);
         const uint32_t zmul = zi * 0x1111u;
         const float lo = kMagic - z, hi = kMagic + 15.0f - z;
-#pragma unroll
-        for (int b = 0; b < E / 8; ++b) {
-            float t[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(u[8 * b + j], inv, kMagic), lo, hi);
-            w[b] = pack8z(t, zmul);
-        }
+        codes_asym<E / 8>([&](int b, int j) { return u[8 * b + j]; }, inv, lo, hi, zmul, umax, umin, w);
         // zero points: group pairs (2i, 2i + 1) -> one byte, written by the
         // first lane of the even group
         uint32_t zn = zi;
@@ -891,6 +922,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
             static_assert(Q0::logg == 7, "one group per row");
             const float f = a.norm;   // y = sig * f * v
             float s, zf = 0.0f;
+            float umax = 0.0f, umin = 0.0f;   // the lane's extremes of v (asymmetric)
             if constexpr (Q0::sym) {
                 float am = fabsf(v[0]);
 #pragma unroll
@@ -906,6 +938,8 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
                     hi = fmaxf(hi, v[j]);
                     nl = fmaxf(nl, -v[j]);
                 }
+                umax = hi;
+                umin = -nl;
                 if (h) {   // the lane holds -y: max y = max(-v), -min y = max v
                     const float t = hi;
                     hi = nl;
@@ -951,13 +985,7 @@ __global__ void __launch_bounds__(256) k128(const FastArgs a) {
                 zi = static_cast<uint32_t>(z);
                 const uint32_t zmul = zi * 0x1111u;
                 const float lo = kMagic - z, hi = kMagic + 15.0f - z;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    float t[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(v[8 * c + j], inv, kMagic), lo, hi);
-                    w[c] = pack8z(t, zmul);
-                }
+                codes_asym<2>([&](int c, int j) { return v[8 * c + j]; }, inv, lo, hi, zmul, umax, umin, w);
                 // rows 2m, 2m + 1 live in lanes 4m, 4m + 2 (q = 0): one byte
                 const uint32_t zodd = dppu<kXor2>(zi);
                 if (valid && qq == 0 && (n & 3) == 0) {
@@ -1047,6 +1075,7 @@ __global__ void __launch_bounds__(256) k128q(const FastArgs a) {
 
     const float f = a.norm;
     float s, zf = 0.0f;
+    float umax = 0.0f, umin = 0.0f;   // the lane's extremes of v (asymmetric)
     if constexpr (Q0::sym) {
         float am = fabsf(v[0]);
 #pragma unroll
@@ -1061,6 +1090,8 @@ __global__ void __launch_bounds__(256) k128q(const FastArgs a) {
             hi = fmaxf(hi, v[j]);
             nl = fmaxf(nl, -v[j]);
         }
+        umax = hi;
+        umin = -nl;
         hi = fmaxf(hi, __shfl_xor(hi, 16));
         nl = fmaxf(nl, __shfl_xor(nl, 16));
         hi = fmaxf(hi, __shfl_xor(hi, 32));
@@ -1098,13 +1129,7 @@ __global__ void __launch_bounds__(256) k128q(const FastArgs a) {
         const uint32_t zi = static_cast<uint32_t>(z);
         const uint32_t zmul = zi * 0x1111u;
         const float lo = kMagic - z, hi = kMagic + 15.0f - z;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float t[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = __builtin_amdgcn_fmed3f(fmaf(v[8 * c + j], inv, kMagic), lo, hi);
-            w[c] = pack8z(t, zmul);
-        }
+        codes_asym<4>([&](int c, int j) { return v[8 * c + j]; }, inv, lo, hi, zmul, umax, umin, w);
         // rows 2m, 2m + 1 live in lanes 2m, 2m + 1 (q = 0): one byte
         const uint32_t zodd = dppu<kXor1>(zi);
         if (valid && qq == 0 && (n & 1) == 0) {
@@ -1256,6 +1281,7 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
                                              int64_t gidx, bool valid, bool first) {
     static_assert(Q::logg == 7, "groups of 128 columns");
     float s, zf = 0.0f;
+    float umax = 0.0f, umin = 0.0f;   // the lane's extremes of u (asymmetric)
     if constexpr (Q::sym) {
         float am = fabsf(u[0]);
 #pragma unroll
@@ -1269,6 +1295,8 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
             hi = fmaxf(hi, u[j]);
             nl = fmaxf(nl, -u[j]);
         }
+        umax = hi;
+        umin = -nl;
         // after the swap, max(hi, nl) is the group's max y in lanes 0-31 and
         // its -min y in lanes 32-63; a second swap hands each to every lane
         swap_halves(hi, nl);
@@ -1304,13 +1332,7 @@ __device__ __forceinline__ uint32_t epi_kron(const float (&u)[64], float f, cons
         const uint32_t zi = static_cast<uint32_t>(z);
         const uint32_t zmul = zi * 0x1111u;
         const float lo = kMagic - z, hi = kMagic + 15.0f - z;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            float t[8];
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq) t[qq] = __builtin_amdgcn_fmed3f(fmaf(u[kron_elem(m, qq)], inv, kMagic), lo, hi);
-            w[m] = pack8z(t, zmul);
-        }
+        codes_asym<8>([&](int m, int qq) { return u[kron_elem(m, qq)]; }, inv, lo, hi, zmul, umax, umin, w);
         zret = zi;
     }
     if (valid) {

@@ -444,6 +444,26 @@ def test_head_dim_rows_ragged_sym(kernel_path, rows):
     run_act(x, 128, 0, hr.QSpec("int", 4, 128, True, "bf16"))
 
 
+@pytest.mark.parametrize("case", [(64, 14336, 2048), (64, 14336, 0), (4096, 128, 0), (48, 13824, 0),
+                                  (96, 4096, 4096)],
+                         ids=["r4-block2048", "kron-28x512", "r3-head128", "kron-108x128", "block4096"])
+def test_asym_clamp_binds(kernel_path, case):
+    # Asymmetric codes are clamp(rne(y / s) + z, 0, 15).  With a bf16 scale a
+    # group's extreme values can round one step past 0 or 15, and the kernels
+    # skip the clamp for waves where no lane's extremes do.  These inputs hold
+    # groups of both kinds; the codes must still match the oracle exactly.
+    rows, n, block = case
+    x = synth.gaussian((rows, n), seed=7100 + n + block, dtype=torch.bfloat16)
+    y = oracle.rotate(x, n, block).reshape(-1, n)
+    ref = oracle.rtn_quant(y, 128, 4, False, "bf16")
+    pre = ref.pre.reshape(rows, n // 128, 128)
+    unclamped = np.rint(pre) + ref.zeros[..., None]
+    binds = ((unclamped < 0) | (unclamped > 15)).any(axis=-1)
+    say("groups where the clamp binds: %d of %d" % (int(binds.sum()), binds.size))
+    assert 0 < binds.sum() < binds.size
+    run_act(x, n, block, hr.QSpec("int", 4, 128, False, "bf16"), ref_y=y)
+
+
 @pytest.mark.parametrize("block", [32, 0])
 def test_mxfp4_activations(kernel_path, block):
     # block-32 rotation with MXFP4 activations (the pages' accuracy setting)
