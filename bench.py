@@ -16,7 +16,7 @@ Reported beside the step (not part of it): tiny, 256 x 128 float32 with
 FWHT 128, int4 sym g32 and the rotated float32 output; its 282,624 bytes take
 35 ns at HBM peak, so its launch time measures latency, not bandwidth.
 
-Measured only when named in --only (not part of the step): r1_mx32 and
+Measured when named in --only (not part of the step): r1_mx32 and
 r4_mx32, the R1 and R4 inputs with a block-32 rotation fused with MXFP4
 (E2M1 codes, one E8M0 scale per block of 32); r1_nv16 and r4_nv16, the same
 inputs with a block-16 rotation fused with NVFP4 (one E4M3 scale per block
@@ -27,7 +27,10 @@ signs, blocks of 2048); down_out, the output-side fusion R1^T W on down_proj
 r4_13824 and r4_17920, R4 at full intermediate widths 12 x 1024, 108 x 128
 and 140 x 128; out_5120 and out_8192, output-side fusion of square weights
 over 5120 (20 x 256) and 8192 rows; r1_8192, R1 at hidden 8192; r4_b1024,
-r4_b256 and r4_b64, the R4 input with blocks of 1024, 256 and 64.
+r4_b256 and r4_b64, the R4 input with blocks of 1024, 256 and 64.  A default
+run (no --only) also times r1_mx32, r1_nv16, r1_random, r4_rpbh, down_out,
+r4_13824 and r4_17920 alone after the step and reports them under
+config.next_rows (not in the value).
 
 The step touches about 2 GB, eight times the 256 MB Infinity Cache, and no
 two launches read the same tensor, so every launch reads its input from HBM.
@@ -70,6 +73,10 @@ PARTS = ("r1", "r4", "r4_kron", "r3_q", "r3_k", "weight")
 EXTRA_PARTS = ("r1_mx32", "r4_mx32", "r1_nv16", "r4_nv16", "r1_random", "r4_rpbh",
                "down_out", "r1_5120", "r4_12288", "r4_13824", "r4_17920", "out_5120",
                "out_8192", "r1_8192", "r4_b1024", "r4_b256", "r4_b64")   # measured only when named in --only
+# one part per row beside the step (block-32 MXFP4, randomised rotations,
+# output-side fusion, NVFP4) and the widest Kronecker base orders: timed alone
+# after the step in a default run, reported under config.next_rows
+NEXT_DEFAULT = ("r1_mx32", "r1_nv16", "r1_random", "r4_rpbh", "down_out", "r4_13824", "r4_17920")
 COPY_BYTES = 256 * 1024 * 1024
 CYCLE_BYTES = 640 * 1024 * 1024   # input copies cycled per part when timing it alone
 
@@ -293,7 +300,8 @@ def time_tiny(hr, synth, torch, stream, launches):
     nbytes = x.numel() * 4 * 2 + qbytes(x.shape[0], w.n, spec)
     return {"ms_median": round(med, 5), "ms_min": round(ms[0], 5), "bytes": nbytes,
             "GB_s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-            "rows_per_s": round(x.shape[0] / (med * 1e-3), 1), "latency_bound": True}
+            "rows_per_s": round(x.shape[0] / (med * 1e-3), 1), "latency_bound": True,
+            "dispatches": 5 + launches}
 
 
 def stream_lib():
@@ -431,6 +439,8 @@ def main():
     ap.add_argument("--only", default=None, help="comma-separated subset of %s (for profiling), or of %s (block-32 MXFP4 "
                          "on the R1 / R4 inputs)" % (",".join(PARTS), ",".join(EXTRA_PARTS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the parts timed beside the step in a default run (%s)" % ",".join(NEXT_DEFAULT))
     ap.add_argument("--cpu-fraction", type=float, default=1.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 256 MiB device copy three times "
@@ -506,6 +516,23 @@ def main():
     if only is None:
         tiny = time_tiny(hr, synth, torch, stream, max(args.steps, 20))
         copy_ref = copy_reference(torch, stream)
+    next_rows = None
+    if only is None and not args.no_next_rows:
+        # beside the step, not part of it: each part alone, back to back over
+        # copies of its input, as the step's parts are timed (before the copy
+        # calibration, whose copies must be the run's last)
+        nparts, _ = build_parts(hr, synth, torch, set(NEXT_DEFAULT))
+        next_rows = {}
+        for nm in NEXT_DEFAULT:
+            ms, copies, launches, floor_ms = time_back_to_back(torch, stream, nparts[nm], min(args.steps, 100), sref)
+            gbs = nparts[nm]["bytes"] / (ms * 1e-3) / 1e9
+            next_rows[nm] = {"ms": round(ms, 5), "bytes": nparts[nm]["bytes"], "GB_s": round(gbs, 1),
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "input_copies": copies, "launches": launches}
+            if floor_ms is not None:
+                next_rows[nm]["stream_floor_ms"] = round(floor_ms, 5)
+                next_rows[nm]["of_stream_floor"] = round(floor_ms / ms, 4)
+        del nparts
+        torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -545,7 +572,7 @@ def main():
         "config": {"workload": "hot-path step: " + " + ".join(names), "bytes_per_step": step_bytes,
                    "rows_per_step": step_rows, "io": "bf16 in; int4/MXFP4 codes, bf16 scales/outputs",
                    "parts": per, "sum_of_parts_ms": round(sum(per[nm]["ms"] for nm in names), 5),
-                   "tiny": tiny, "copy_reference": copy_ref,
+                   "tiny": tiny, "copy_reference": copy_ref, "next_rows": next_rows,
                    "valu_clock_mhz": {"before_timed_steps": clock_before, "after_timed_steps": clock_after}},
         "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

@@ -87,10 +87,22 @@ def cmd_trace(argv):
             n, len(p["step"]) + len(p["b2b"]) + len(p["event"]), statistics.mean(p["step"]), statistics.mean(p["b2b"]),
             statistics.mean(p["event"]), min(p["b2b"]), p["kernel"][:110]))
     tail = rows[len(seq):]
+    tiny = d["config"].get("tiny") or {}
+    ntiny = tiny.get("dispatches", len(tail))
     if tail:
-        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in tail]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in tail[:ntiny]]
         print("tiny     %6d %12s %12.2f %12s %10.2f  %s" % (len(durs), "-", statistics.median(durs), "-", min(durs),
                                                            tail[0]["Kernel_Name"][:110]))
+    # parts timed beside the step (config.next_rows): each alone, back to
+    # back over copies of its input (the first input_copies launches untimed)
+    rest = tail[ntiny:]
+    for n, p in (d["config"].get("next_rows") or {}).items():
+        k0, k = p["input_copies"], p["launches"]
+        mine, rest = rest[:k0 + k], rest[k0 + k:]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in mine[k0:]]
+        if durs:
+            print("%-8s %6d %12s %12.2f %12s %10.2f  %s" % (n, len(durs), "-", statistics.mean(durs), "-", min(durs),
+                                                            mine[-1]["Kernel_Name"][:110]))
     print("bench: value %.1f GB/s, ms_per_step %.5f, sum of parts (alone, back to back) %.5f ms, warm-up %d steps "
           "in %.2f s" % (d["value"], d["ms_per_step"], d["config"]["sum_of_parts_ms"], d["warmup_steps_run"],
                          d["warmup_s"]))
