@@ -97,6 +97,8 @@ def cmd_trace(argv):
     # back over copies of its input (the first input_copies launches untimed)
     rest = tail[ntiny:]
     for n, p in (d["config"].get("next_rows") or {}).items():
+        if not isinstance(p, dict):
+            continue   # "error": those parts were not measured
         k0, k = p["input_copies"], p["launches"]
         mine, rest = rest[:k0 + k], rest[k0 + k:]
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in mine[k0:]]
