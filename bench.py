@@ -48,8 +48,8 @@ rest of its algorithmic bytes: stream_floor_ms is what a launch of that shape
 takes here with no computation, and of_stream_floor = stream_floor_ms / ms.
 Each part's single-launch time
 inside K more steps, an event pair around every launch, is reported too
-(ms_single: it adds the events' few microseconds, which matter for the 42 MB
-R1 launch).  copy_reference times the runtime's 256 MiB device copy the same
+(ms_single, the mean, with ms_single_median and ms_single_min: it adds the
+events' few microseconds, which matter for the 42 MB R1 launch).  copy_reference times the runtime's 256 MiB device copy the same
 way, as a reference point.  valu_clock_mhz is the shader clock measured
 right before and right after the timed steps (an FMA issue-rate probe in
 libhrstream.so): boxes of this model run at different clocks, which moves the
@@ -553,12 +553,14 @@ def main():
     per = {}
     for nm in names:
         ms, copies, launches, floor_ms = b2b[nm]
-        ms_single = sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps
+        singles = sorted(a.elapsed_time(b) for a, b in ev[nm])
+        ms_single = sum(singles) / args.steps
         gbs = parts[nm]["bytes"] / (ms * 1e-3) / 1e9
         per[nm] = {"ms": round(ms, 5), "bytes": parts[nm]["bytes"], "GB_s": round(gbs, 1),
                    "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_per_s": round(parts[nm]["rows"] / (ms * 1e-3), 1),
                    "input_copies": copies, "launches": launches, "ms_single": round(ms_single, 5),
-                   "frac_single": round(parts[nm]["bytes"] / (ms_single * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "frac_single": round(parts[nm]["bytes"] / (ms_single * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "ms_single_median": round(singles[len(singles) // 2], 5), "ms_single_min": round(singles[0], 5)}
         if floor_ms is not None:
             per[nm]["stream_floor_ms"] = round(floor_ms, 5)
             per[nm]["stream_floor_frac"] = round(parts[nm]["bytes"] / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
