@@ -770,6 +770,29 @@ def test_weight_out_tall_and_kronecker(out_f, in_f, block, dt):
     say("  ", rep)
 
 
+@pytest.mark.parametrize("in_f,in_place", [(1032, False), (2400, False), (4096, False), (4096, True)])
+def test_weight_out_8192_bf16(in_f, in_place):
+    """bf16 over 8192 rows on wider weights: 258, 600 and 1024 tiles of 4
+    columns (more than one per workgroup of the persistent grid; 258 is not a
+    multiple of 8, so no XCD grouping), and in place.  The first 16 and last 8
+    columns and a sample of others are compared with the oracle."""
+    out_f = 8192
+    w = synth.make_inputs(synth.WORKLOADS["weight"], out_features=out_f, in_features=in_f)
+    w[:, 9] = 0.0
+    say("rotate_fuse_weight_out", out_f, in_f, 0, "bf16", "in place" if in_place else "")
+    wg = w.to(DEV)
+    wr = hr.rotate_fuse_weight_out(wg, 0, out=wg if in_place else None)
+    torch.cuda.synchronize()
+    if in_place:
+        assert wr.data_ptr() == wg.data_ptr()
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(in_f - 8, in_f),
+                                     np.random.default_rng(in_f).choice(in_f, size=48, replace=False)]))
+    ref = oracle.rotate_out(w[:, torch.as_tensor(cols)], out_f, 0)
+    rep = Report()
+    check_rotated(to_np64(wr)[:, cols].T.copy(), ref.T.copy(), "bf16", rep)
+    say("  ", rep)
+
+
 def test_weight_out_in_place_and_layer_equivalence():
     """In place, and the fused weight reproduces the rotated layer output:
     x . W'^T against (x . W^T) . R on the GPU-rounded weight."""
